@@ -1,0 +1,64 @@
+// Internal helpers shared by the HIP sources of libhp (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/hp.h"
+
+namespace hp {
+
+// Thread-local error text behind hp_last_error().
+hp_status fail(hp_status st, const char* fmt, ...);
+// Checks a HIP runtime result; sets the error text on failure.
+hp_status hip_ok(hipError_t e, const char* what);
+// Checks the last launch on this thread.
+hp_status launch_ok(const char* kernel);
+
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- launchers implemented in the .hip files (all enqueue on `st`) ----
+void launch_quantize_g64(const void* x, int64_t rows, int64_t cols, void* codes, void* sm,
+                         hipStream_t st);
+void launch_dequantize_g64(const void* codes, const void* sm, int64_t rows, int64_t cols, void* y,
+                           hipStream_t st);
+void launch_pack_q4(const void* codes, const void* sm, int32_t k, int32_t n, void* packed,
+                    void* scale, void* minv, hipStream_t st);
+void launch_pack_f16(const void* w, int32_t k, int32_t n, void* wt, hipStream_t st);
+
+// GEMM: y = act(x·w) + res (see hp_gemm).  ws holds split-K partials.
+size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n);
+hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, const void* res,
+                      int64_t ldr, bool relu, void* y, int64_t ldy, void* ws, hipStream_t st);
+
+// KV append / attention.  `dpos` (device int32, may be NULL): when set, the
+// kernels read pos from it (plus pos as an offset), so a captured graph can
+// be replayed at advancing positions.
+void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
+                      int32_t pos, const int32_t* dpos, const hp_kv& kv, hipStream_t st);
+void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, const void* qkv,
+                              void* out, hipStream_t st);
+void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
+                             int32_t pos, const int32_t* dpos, const uint64_t* masks,
+                             const hp_kv& kv, void* out, hipStream_t st);
+void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
+                       hipStream_t st);
+
+// Small utility kernels used by the block runner.
+void launch_copy_step(const void* src, int64_t count_elems, int64_t stride_elems,
+                      const int32_t* dstep, void* dst, int direction, hipStream_t st);
+void launch_add_i32(int32_t* p, int32_t v, hipStream_t st);
+
+}  // namespace hp

@@ -1,0 +1,255 @@
+/*
+ * hp.h -- C ABI of the MI355X (gfx950) hot path for the FlexGen OPT-style
+ * transformer layer with group-wise int4 compression.
+ *
+ * Sources cited below:
+ *   [FlexGen]  paper notes "FlexGen: High-Throughput Generative Inference of
+ *              Large Language Models with a Single GPU" (ICML 2023).
+ *   [SpecPipe] article "大语言模型推理加速：SpecPipe技术解析与实践".
+ *
+ * Notation follows [FlexGen] (background section): b requests, prompt length
+ * s, n generated tokens, hidden size h1, MLP size h2, l layers.  heads splits
+ * h1 into heads of d = h1/heads channels; gbs is the GPU batch size of the
+ * block schedule ([FlexGen] section 4, block size = gbs x number of GPU
+ * batches).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named dev_* or documented as device memory point to device
+ *    memory on the current HIP device; descriptor structs (hp_dims, hp_mat,
+ *    hp_layer, hp_kv) live in host memory and are read during the call only.
+ *  - The caller owns and frees all device memory.  No entry point allocates
+ *    device memory except hp_run_block with HP_GRAPH (it keeps one captured
+ *    graph per argument set until hp_release_graphs()).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns without waiting, unless stated otherwise.
+ *  - Argument errors are detected on the host before anything is enqueued:
+ *    the call returns a negative hp_status and hp_last_error() describes it
+ *    (thread-local text).  HP_ERR_HIP reports a HIP runtime error at launch;
+ *    errors raised later by the device surface at the caller's next sync.
+ *  - binary16 tensors are IEEE 754 half precision; row-major throughout.
+ *  - Results do not depend on gbs or on the schedule order: every row's sums
+ *    are reduced in an order fixed by the matrix shapes alone.
+ *  - The device must be gfx950 (HP_ERR_DEVICE otherwise).
+ */
+#ifndef HP_H_
+#define HP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HP_OK = 0,
+  HP_ERR_NULL = -1,      /* a required pointer is NULL */
+  HP_ERR_SHAPE = -2,     /* sizes violate a documented rule */
+  HP_ERR_CAPACITY = -3,  /* cache rows [pos, pos+q) do not fit in cap */
+  HP_ERR_TREE = -4,      /* tree arguments out of range */
+  HP_ERR_WORKSPACE = -5, /* workspace smaller than hp_workspace_bytes() */
+  HP_ERR_DEVICE = -6,    /* no device, or the device is not gfx950 */
+  HP_ERR_HIP = -7        /* a HIP runtime call failed */
+} hp_status;
+
+/* Storage formats. */
+enum { HP_F16 = 0, HP_Q4 = 1 };
+
+/*
+ * Group-wise asymmetric int4 ([FlexGen] section 5, group-wise quantization):
+ * a group is 64 consecutive elements along one dimension; each element is
+ * coded as c = round((x - min) / (max - min) * 15) and read back as
+ * fp16(c * scale + min).  Exact definition used here (the page gives the
+ * real-number formula only):
+ *   - x is the fp16 value as binary32, with -0 taken as +0;
+ *   - min/max skip NaN (IEEE minNum/maxNum); r = max - min in binary32;
+ *   - if !(r > 0): every code 0, scale = +0, min = fp16(min) (+0 if no finite
+ *     element);
+ *   - else scale = fp16(r / 15), min = fp16(min), and
+ *     c = clamp(rint(((x - min) / r) * 15), 0, 15) in binary32 with
+ *     correctly rounded division and round-half-to-even rint (NaN -> 0);
+ *   - dequantised value: fp16(c * scale + min) with a single rounding.
+ * Generic ("row") layout, used for the KV cache and hp_quantize_g64:
+ *   codes u8[rows][cols/2], byte j of a group = c[2j] | c[2j+1] << 4;
+ *   sm = half2 {scale, min} [rows][cols/64].
+ */
+
+/*
+ * Weight matrix w in[h_in = k][h_out = n] of the product x·w ([FlexGen]
+ * background section).  Weights are grouped along the output-channel
+ * dimension ([FlexGen] section 5): a group is w[kk][64 g .. 64 g + 63].
+ * Stored in the GEMM layout produced by hp_pack_weight_*:
+ *   HP_F16: data = half wt[n][k] (the transpose: k contiguous per output).
+ *   HP_Q4:  data = u8 tiles[n/16][k/128][64][16]: tile (nb, kb), lane L
+ *           (0..63) holds the 32 codes of output column n = 16 nb + L % 16
+ *           at inputs kk = 128 kb + 32 (L / 16) + 0..31, as 4 dwords; dword
+ *           j holds kk-offsets 8 j + e, e = 0..7, with offset e in nibble
+ *           (e even ? e / 2 : 4 + e / 2) (bits 4*nibble .. 4*nibble+3);
+ *           scale = half [n/64][k], minv = half [n/64][k] (per group).
+ *   Requires k % 128 == 0 and n % 64 == 0.
+ */
+typedef struct {
+  int32_t fmt;       /* HP_F16 or HP_Q4 */
+  int32_t k, n;      /* h_in, h_out */
+  const void* data;  /* device */
+  const void* scale; /* device, HP_Q4 only (else NULL) */
+  const void* minv;  /* device, HP_Q4 only (else NULL) */
+} hp_mat;
+
+/* One layer.  wqkv is [h1 -> 3 h1] with output columns Q | K | V (the
+ * concatenation of w_Q, w_K, w_V); wo [h1 -> h1]; w1 [h1 -> h2];
+ * w2 [h2 -> h1].  All four use the same fmt. */
+typedef struct {
+  hp_mat wqkv, wo, w1, w2;
+} hp_layer;
+
+/* One layer's KV cache ([FlexGen] decode equations: rows grow by Concat;
+ * section 5: KV grouped along the hidden dimension).  Head-major:
+ *   HP_F16: k, v = half [b][heads][cap][d];  k_sm = v_sm = NULL.
+ *   HP_Q4:  k, v = u8 codes [b][heads][cap][d/2] (generic row layout, one
+ *           row = one token of one head, groups of 64 channels),
+ *           k_sm, v_sm = half2 {scale, min} [b][heads][cap][d/64].
+ * All pointers are device memory; b is the request count of the call. */
+typedef struct {
+  int32_t fmt, cap;
+  void *k, *v, *k_sm, *v_sm;
+} hp_kv;
+
+typedef struct {
+  int32_t b, s, n, h1, h2, l, heads, gbs;
+} hp_dims;
+/* Shape rules checked by every layer/block entry point: all sizes > 0;
+ * h1 % heads == 0 with d = h1/heads in {64, 128}; h1 % 128 == 0;
+ * h2 % 128 == 0; b % gbs == 0; weights and cache formats consistent with
+ * the dims. */
+
+/* ------------------------------------------------------------ diagnostics */
+const char* hp_last_error(void);
+/* 0 if the current device is gfx950 and usable, else HP_ERR_DEVICE. */
+hp_status hp_device_check(void);
+
+/* ---------------------------------------------------------- compression */
+/* [FlexGen] section 5.  x: device half[rows][cols], groups of 64 along cols
+ * (cols % 64 == 0, rows >= 0).  Writes codes (device u8[rows][cols/2]) and
+ * sm (device half2[rows][cols/64]) in the generic layout above. */
+hp_status hp_quantize_g64(const void* x, int64_t rows, int64_t cols, void* codes, void* sm,
+                          void* stream);
+
+/* [FlexGen] section 5 (converted back to FP16 before computation).
+ * y: device half[rows][cols] = fp16(c * scale + min), single rounding. */
+hp_status hp_dequantize_g64(const void* codes, const void* sm, int64_t rows, int64_t cols,
+                            void* y, void* stream);
+
+/* Rearranges a quantised weight w[k][n] (generic layout: codes u8[k][n/2],
+ * sm half2[k][n/64], groups along n) into the HP_Q4 GEMM layout (packed
+ * tiles, scale, minv; see hp_mat).  Codes are moved, never recomputed. */
+hp_status hp_pack_weight_q4(const void* codes, const void* sm, int32_t k, int32_t n,
+                            void* packed, void* scale, void* minv, void* stream);
+
+/* fp16 weight w[k][n] (device) -> the HP_F16 GEMM layout wt[n][k]. */
+hp_status hp_pack_weight_f16(const void* w, int32_t k, int32_t n, void* wt, void* stream);
+
+/* ---------------------------------------------------------- layer stages */
+/* y[M][n] = fp16(act(x·w) + res): x device half [M][k] (row stride ldx),
+ * w in GEMM layout, res device half [M][n] (row stride ldr) or NULL,
+ * act = ReLU if relu != 0.  y row stride ldy.  Sums in binary32 over k in an
+ * order fixed by (k, n).  [FlexGen] background section: every projection
+ * and MLP product of the layer is such a product.  ws: device scratch of at
+ * least hp_gemm_workspace_bytes(M, k, n) bytes (may be NULL when that is 0). */
+size_t hp_gemm_workspace_bytes(int64_t M, int32_t k, int32_t n);
+hp_status hp_gemm(const void* x, int64_t ldx, const hp_mat* w, int64_t M, const void* res,
+                  int64_t ldr, int32_t relu, void* y, int64_t ldy, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* [FlexGen] decode equations (Concat) and section 5 (KV grouped along the
+ * hidden dimension): for each request r < b and new token i < q, copies (or
+ * quantises) the K and V rows of token i into cache rows pos + i.
+ * qkv: device half [b][q][3 h1] with K at columns [h1, 2 h1) and V at
+ * [2 h1, 3 h1).  Requires pos + q <= kv->cap. */
+hp_status hp_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
+                       int32_t pos, const hp_kv* kv, void* stream);
+
+/* Causal prefill attention over the fresh K/V ([FlexGen] prefill equations;
+ * causal mask: query i sees keys 0..i).  qkv: device half [b][s][3 h1]
+ * (Q | K | V columns); out: device half [b][s][h1]. */
+hp_status hp_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, const void* qkv,
+                               void* out, void* stream);
+
+/* Decode attention over the cache ([FlexGen] decode equations; [SpecPipe]
+ * 2.2.1-2.2.2 for tree masks).  For request r and new token i < q (its K/V
+ * already appended at row pos + i), query i reads, through the stored
+ * format, cache rows [0, pos) and each row pos + u with bit u of
+ * masks[r][i] set; masks == NULL means a chain (rows pos .. pos + i).
+ * q in [1, 64].  qkv: device half [b][q][3 h1] (the query is read from
+ * columns [0, h1)); masks: device uint64 [b][q] or NULL; out: device half
+ * [b][q][h1].  Requires pos + q <= kv->cap. */
+hp_status hp_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
+                              int32_t pos, const uint64_t* masks, const hp_kv* kv, void* out,
+                              void* stream);
+
+/* [SpecPipe] 2.2.1 (tree mask M): builds masks[r][i] (bit u set iff token u
+ * is token i or one of its ancestors) from a BFS parent array per request:
+ * parent: device int32 [b][q], parent[r][0] == -1 and
+ * 0 <= parent[r][i] < i for i > 0.  err: device int32, set to the number of
+ * parent entries that break these rules (their masks hold only the token
+ * itself).  q in [1, 64]. */
+hp_status hp_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks,
+                        int32_t* err, void* stream);
+
+/* ------------------------------------------------------------- layers */
+/* Workspace for hp_layer_prefill / hp_layer_decode / hp_run_block with these
+ * dims (bytes of device memory, 256-byte aligned by the caller). */
+size_t hp_workspace_bytes(const hp_dims* d);
+
+/* One layer, prefill ([FlexGen] background section, prefill equations):
+ * x device half [b][s][h1] -> x_out device half [b][s][h1]; writes cache
+ * rows [0, s) of every request (d->b requests).  Requires s <= kv->cap. */
+hp_status hp_layer_prefill(const hp_dims* d, const hp_layer* w, const void* x, const hp_kv* kv,
+                           void* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/* One layer, decode ([FlexGen] decode equations): t device half
+ * [b][q][h1] at cache rows [pos, pos + q) -> t_out device half [b][q][h1].
+ * masks as in hp_decode_attention (NULL: chain; q == 1 is the plain
+ * decode step).  Requires pos + q <= kv->cap and q <= 64. */
+hp_status hp_layer_decode(const hp_dims* d, const hp_layer* w, const void* t, int32_t pos,
+                          int32_t q, const uint64_t* masks, const hp_kv* kv, void* t_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------- block schedule */
+enum {
+  HP_GRAPH = 1,      /* capture one decode column as a hipGraph, replay it n times */
+  HP_ROW_BY_ROW = 2, /* row-by-row order: each GPU batch runs all steps alone */
+  HP_MICROBATCH = 4  /* zig-zag with one launch per GPU batch (gbs rows)
+                        instead of one launch per block */
+};
+
+/* [FlexGen] section 4, Algorithm 1: zig-zag block schedule over one block of
+ * d->b = gbs x (b/gbs) requests.  Step 0 is the prefill column over x
+ * (device half [b][s][h1]); steps 1..n are decode columns fed the given
+ * embeddings t_in (device half [n][b][h1]; the pages define no token
+ * sampling).  Within a step, layer j runs for the whole block before layer
+ * j + 1, so each layer's weights are read once per step for the block.
+ * layers: host array of d->l hp_layer; kv: host array of d->l hp_kv with
+ * cap >= s + n.  Outputs: x_out device half [b][s][h1] (last layer, prefill)
+ * and t_out device half [n][b][h1] (last layer, each decode step).
+ * times_ms: NULL, or a host float[2] that receives the prefill and decode
+ * durations measured with HIP events on `stream` (the call then waits for
+ * the stream before returning). */
+hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, const void* t_in,
+                       const hp_kv* kv, void* x_out, void* t_out, void* ws, size_t ws_bytes,
+                       uint32_t flags, float* times_ms, void* stream);
+
+/* Drops every captured graph (device memory of graph execs is released). */
+void hp_release_graphs(void);
+
+/* ------------------------------------------------------------ sizes */
+/* [FlexGen] background section (memory bottleneck analysis): weight bytes
+ * l(8 h1^2 + 4 h1 h2) in fp16, and peak KV bytes 4 b l h1 (s + n) in fp16;
+ * fmt HP_Q4 gives the packed sizes (codes plus fp16 scale/min per group). */
+uint64_t hp_weight_bytes(const hp_dims* d, int32_t fmt);
+uint64_t hp_kv_bytes(const hp_dims* d, int32_t fmt);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HP_H_ */

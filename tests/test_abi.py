@@ -1,0 +1,59 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point declared in include/hp.h, and its size helpers reproduce
+the closed forms printed in the FlexGen paper notes (background section)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "hp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_matches_exports():
+    from decode_step_transformer_amd import hp
+    names = _declared()
+    assert names, "no declarations found"
+    assert sorted(hp.EXPORTS) == names
+    L = hp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_flexgen_size_closed_forms():
+    from decode_step_transformer_amd import hp
+    g = {}
+    for ln in open(os.path.join(ROOT, "tests", "golden", "flexgen_sizes.txt")):
+        if ln.startswith("#") or ":" not in ln:
+            continue
+        k, v = ln.split(":")
+        g[k.strip()] = float(v)
+    d = hp.dims(int(g["b"]), int(g["s"]), int(g["n"]), int(g["h1"]), int(g["h2"]), int(g["l"]), 96)
+    w = hp.hp_weight_bytes(d, hp.HP_F16)
+    kv = hp.hp_kv_bytes(d, hp.HP_F16)
+    assert round(w / 1e9) == pytest.approx(g["weights_GB_printed"], abs=25)  # 347.9e9 B = 324 GiB
+    assert round(w / 2 ** 30) == g["weights_GB_printed"] - 1
+    assert round(kv / 2 ** 40, 1) == g["kv_TB_printed"]
+    assert round(kv / w, 1) == g["ratio_printed"]
+    # int4 group-64 packing: 4 bits per element plus 2 x fp16 per 64 elements
+    elems = w // 2
+    assert hp.hp_weight_bytes(d, hp.HP_Q4) == elems // 2 + elems // 64 * 4
+
+
+def test_argument_errors_before_device():
+    """Shape errors are reported on the host before any device work."""
+    from decode_step_transformer_amd import hp
+    L = hp.lib()
+    assert L.hp_quantize_g64(None, 4, 100, None, None, None) == -2      # cols % 64
+    assert L.hp_tree_masks(1, 65, None, None, None, None) == -4         # q > 64
+    d = hp.dims(4, 32, 8, 256, 1024, 2, 3)                              # 256 % 3 != 0
+    assert hp.hp_workspace_bytes(d) == 0
+    d = hp.dims(4, 32, 8, 256, 1024, 2, 4, 3)                           # b % gbs != 0
+    assert hp.hp_workspace_bytes(d) == 0
+    d = hp.dims(4, 32, 8, 256, 1024, 2, 4)
+    assert hp.hp_workspace_bytes(d) > 0

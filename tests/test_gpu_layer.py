@@ -1,0 +1,158 @@
+"""GPU parity of whole layers and of the block schedule against the oracle.
+
+FlexGen paper notes, background section (prefill and decode equations of a
+layer) and section 4 (Algorithm 1, the zig-zag block schedule); section 5
+(int4 group-64 weights and KV cache).  Full-stack comparison on the Tiny
+configuration; per-layer comparisons on multi-tile shapes.
+"""
+import numpy as np
+import pytest
+
+import synth
+from configs import CONFIGS, decode_inputs, layer_weights, oracle_weights, prompt
+from helpers import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hp():
+    import torch
+    from decode_step_transformer_amd import hp as _hp
+    assert torch.cuda.is_available()
+    assert _hp.hp_device_check() == 0, _hp.hp_last_error()
+    return _hp
+
+
+def _gpu_layer(hp, W, fmt):
+    return hp.make_layer({k: dev(v) for k, v in W.items()}, fmt)
+
+
+def _compare_cache(orc, kv_gpu, kv_ref, T, what):
+    if kv_ref.fmt == 0:
+        for w in ("k", "v"):
+            assert_close(host(getattr(kv_gpu, w))[:, :, :T].view(np.float16),
+                         getattr(kv_ref, w)[:, :, :T].view(np.float16), what=f"{what} {w}")
+        return
+    for w in ("k", "v"):
+        g = host(getattr(kv_gpu, w))[:, :, :T]
+        r = getattr(kv_ref, w)[:, :, :T]
+        # codes come from fp16 K/V produced by differently ordered sums: they
+        # may differ where a value sits at a rounding or code boundary, by one
+        # code; dequantised values must agree within the tolerance.
+        eq = (g == r).mean()
+        assert eq > 0.995, f"{what} {w}: only {eq:.4f} of code bytes equal"
+        gv = orc.dequantize_g64(g, host(getattr(kv_gpu, w + "_sm"))[:, :, :T])
+        rv = kv_ref.values(w, T)
+        assert_close(gv, rv, what=f"{what} {w} dequantised")
+
+
+@pytest.mark.parametrize("w_fmt,kv_fmt", [(0, 0), (1, 1), (1, 0)])
+@pytest.mark.parametrize("heads", [2, 4])
+def test_layer_prefill_then_decode(hp, orc, w_fmt, kv_fmt, heads):
+    import torch
+    b, s, n, h1, h2 = 3, 40, 3, 256, 512
+    D = h1 // heads
+    W = layer_weights(77, 0, h1, h2, 0.05)
+    Wo = oracle_weights(orc, W, w_fmt)
+    layer = _gpu_layer(hp, W, w_fmt)
+    x = prompt(77, b, s, h1)
+    d = hp.dims(b, s, n, h1, h2, 1, heads)
+    ws = torch.empty(hp.hp_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    kv = hp.KVCache(kv_fmt, b, heads, s + n, D)
+    y = torch.empty((b, s, h1), dtype=torch.float16, device="cuda")
+    hp.hp_layer_prefill(d, layer, dev(x), kv, y, ws)
+    kref = orc.KV(kv_fmt, b, heads, s + n, D)
+    yref = orc.layer_prefill(x, Wo, kref, heads)
+    assert_close(host(y), yref, what="prefill")
+    _compare_cache(orc, kv, kref, s, "prefill cache")
+    for i in range(n):
+        t = synth.normal_f16(synth.seed_for(77), 500 + i, (b, 1, h1))
+        to = torch.empty((b, 1, h1), dtype=torch.float16, device="cuda")
+        hp.hp_layer_decode(d, layer, dev(t), s + i, 1, kv, to, ws)
+        tref = orc.layer_decode(t, Wo, kref, heads, s + i)
+        assert_close(host(to), tref, what=f"decode step {i}")
+    _compare_cache(orc, kv, kref, s + n, "decode cache")
+
+
+def test_layer_decode_tree(hp, orc):
+    """q = 16 tree tokens per request with BFS parent masks."""
+    import torch
+    b, s, q, h1, h2, heads = 2, 20, 16, 256, 256, 2
+    W = layer_weights(78, 0, h1, h2, 0.05)
+    Wo = oracle_weights(orc, W, 1)
+    layer = _gpu_layer(hp, W, 1)
+    d = hp.dims(b, s, 1, h1, h2, 1, heads)
+    ws = torch.empty(hp.hp_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    x = prompt(78, b, s, h1)
+    kv = hp.KVCache(1, b, heads, s + q, h1 // heads)
+    kref = orc.KV(1, b, heads, s + q, h1 // heads)
+    y = torch.empty((b, s, h1), dtype=torch.float16, device="cuda")
+    hp.hp_layer_prefill(d, layer, dev(x), kv, y, ws)
+    orc.layer_prefill(x, Wo, kref, heads)
+    parents = np.stack([synth.bfs_parents(synth.seed_for(78), r, q) for r in range(b)])
+    masks, err = hp.hp_tree_masks(dev(parents.astype(np.int32)))
+    t = synth.normal_f16(synth.seed_for(78), 600, (b, q, h1))
+    to = torch.empty((b, q, h1), dtype=torch.float16, device="cuda")
+    hp.hp_layer_decode(d, layer, dev(t), s, q, kv, to, ws, masks=masks)
+    mref = np.stack([orc.tree_masks(p) for p in parents])
+    tref = orc.layer_decode(t, Wo, kref, heads, s, mref)
+    assert_close(host(to), tref, what="tree decode")
+
+
+def _tiny_setup(hp, orc):
+    import torch
+    c = CONFIGS[1]
+    l, h1, h2, heads, b, s, n = c["l"], c["h1"], c["h2"], c["heads"], c["b"], c["s"], c["n"]
+    Ws = [layer_weights(1, j, h1, h2) for j in range(l)]
+    layers = [_gpu_layer(hp, W, 1) for W in Ws]
+    x = prompt(1, b, s, h1)
+    t = decode_inputs(1, n, b, h1)
+    return c, Ws, layers, x, t
+
+
+def _run_gpu_block(hp, c, layers, x, t, gbs, flags):
+    import torch
+    b, s, n, h1, heads = c["b"], c["s"], c["n"], c["h1"], c["heads"]
+    d = hp.dims(b, s, n, h1, c["h2"], c["l"], heads, gbs)
+    ws = torch.empty(hp.hp_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    kvs = [hp.KVCache(1, b, heads, s + n, h1 // heads) for _ in layers]
+    xo = torch.empty((b, s, h1), dtype=torch.float16, device="cuda")
+    to = torch.empty((n, b, h1), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        hp.hp_run_block(d, layers, dev(x), dev(t), kvs, xo, to, ws, flags, stream=stream)
+    stream.synchronize()
+    return host(xo), host(to), [(host(k.k), host(k.v)) for k in kvs]
+
+
+def test_tiny_block_vs_oracle(hp, orc):
+    c, Ws, layers, x, t = _tiny_setup(hp, orc)
+    xo, to, _ = _run_gpu_block(hp, c, layers, x, t, c["b"], hp.HP_GRAPH)
+    Wo = [oracle_weights(orc, W, 1) for W in Ws]
+    kref = [orc.KV(1, c["b"], c["heads"], c["s"] + c["n"], c["h1"] // c["heads"]) for _ in Ws]
+    rx, rt = orc.run_block(x, t, Wo, kref, c["heads"], c["b"])
+    assert_close(xo, rx, what="tiny prefill output")
+    assert_close(to, rt, what="tiny decode outputs")
+
+
+def test_tiny_block_schedules_bitwise(hp, orc):
+    """Graph replay, eager launches, per-GPU-batch launches and row-by-row
+    order all give bitwise-identical outputs and caches."""
+    c, Ws, layers, x, t = _tiny_setup(hp, orc)
+    ref = _run_gpu_block(hp, c, layers, x, t, c["b"], hp.HP_GRAPH)
+    for gbs, flags in ((c["b"], 0), (2, hp.HP_MICROBATCH), (2, hp.HP_ROW_BY_ROW),
+                       (1, hp.HP_ROW_BY_ROW), (2, hp.HP_MICROBATCH | hp.HP_GRAPH)):
+        got = _run_gpu_block(hp, c, layers, x, t, gbs, flags)
+        assert np.array_equal(got[0].view(np.uint16), ref[0].view(np.uint16)), (gbs, flags)
+        assert np.array_equal(got[1].view(np.uint16), ref[1].view(np.uint16)), (gbs, flags)
+        for (a, b_), (ra, rb) in zip(got[2], ref[2]):
+            assert np.array_equal(a, ra) and np.array_equal(b_, rb)
+
+
+def test_graph_replays_repeat(hp, orc):
+    """A cached graph replayed by a second call gives the same outputs."""
+    c, Ws, layers, x, t = _tiny_setup(hp, orc)
+    a = _run_gpu_block(hp, c, layers, x, t, c["b"], hp.HP_GRAPH)
+    b_ = _run_gpu_block(hp, c, layers, x, t, c["b"], hp.HP_GRAPH)
+    assert np.array_equal(a[1].view(np.uint16), b_[1].view(np.uint16))
