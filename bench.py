@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the FlexGen OPT-style layer stack on one MI355X.
+
+One step = one block through hp_run_block: the prefill column over the
+prompt, then n decode columns (each a hipGraph replay), every layer of the
+stack, with int4 group-64 weights and KV cache resident in HBM (FlexGen
+paper notes: background section for the layer, section 4 / Algorithm 1 for
+the zig-zag block schedule, section 5 for the compression).
+
+Metric: generated tokens/s = b*n / decode time of the block (the prefill-
+inclusive rate b*n / (prefill + decode) is reported beside it).  Inputs and
+weights are seeded synthetic tensors of the configuration's shapes.
+
+Prints one JSON line (rank 0, N = 1 only):
+  roofline      -- the dominant kernel of the timed region, timed with HIP
+                   events on its own stream through hp_profile, against the
+                   published MI355X peak for its bound;
+  decode_kernels-- the same for the decode-phase kernels (one eager decode
+                   column after the timed region);
+  cpu_baseline  -- the CPU oracle timed on a bounded sample of the same
+                   workload (one decode layer for a few requests).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+CONFIGS = {
+    "tiny": dict(l=2, h1=256, h2=1024, heads=4, b=4, gbs=4, s=32, n=8, fmt=1),
+    "opt-6.7b-fp16": dict(l=32, h1=4096, h2=16384, heads=32, b=64, gbs=64, s=512, n=32, fmt=0),
+    "opt-30b-int4": dict(l=48, h1=7168, h2=28672, heads=56, b=144, gbs=48, s=512, n=32, fmt=1),
+    "opt-175b-int4": dict(l=96, h1=12288, h2=49152, heads=96, b=144, gbs=48, s=512, n=32, fmt=1),
+}
+CONFIG_SEED = {"tiny": 1, "opt-6.7b-fp16": 2, "opt-30b-int4": 3, "opt-175b-int4": 4}
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_flops(c, M):
+    h1, h2 = c["h1"], c["h2"]
+    return 2.0 * M * (4 * h1 * h1 + 2 * h1 * h2)
+
+
+def weight_bytes_per_layer(c):
+    elems = 4 * c["h1"] ** 2 + 2 * c["h1"] * c["h2"]
+    return elems * (0.5 + 4 / 64) if c["fmt"] == 1 else elems * 2.0
+
+
+def kv_bytes_read(c, T):
+    """Cache bytes one decode attention launch must read: K and V rows [0, T)."""
+    per_row = c["h1"] * (0.5 + 4 / 64) if c["fmt"] == 1 else c["h1"] * 2.0
+    return 2.0 * c["b"] * T * per_row
+
+
+def setup(c, seed, hp, torch):
+    dev = "cuda"
+    l, h1, h2, heads, b, s, n = c["l"], c["h1"], c["h2"], c["heads"], c["b"], c["s"], c["n"]
+    g = torch.Generator(device=dev)
+    layers = []
+    for j in range(l):
+        g.manual_seed(seed * 1000 + j)
+        W = {}
+        for name, shp in (("wq", (h1, h1)), ("wk", (h1, h1)), ("wv", (h1, h1)), ("wo", (h1, h1)),
+                          ("w1", (h1, h2)), ("w2", (h2, h1))):
+            W[name] = (torch.randn(shp, generator=g, device=dev, dtype=torch.float32) * 0.02).half()
+        layers.append(hp.make_layer(W, c["fmt"]))
+        del W
+    g.manual_seed(seed * 1000 + 999)
+    x = torch.randn((b, s, h1), generator=g, device=dev, dtype=torch.float32).half()
+    t_in = torch.randn((n, b, h1), generator=g, device=dev, dtype=torch.float32).half()
+    kvs = [hp.KVCache(c["fmt"], b, heads, s + n, h1 // heads, device=dev) for _ in range(l)]
+    d = hp.dims(b, s, n, h1, h2, l, heads, c["gbs"])
+    ws = torch.empty(hp.hp_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    x_out = torch.empty_like(x)
+    t_out = torch.empty_like(t_in)
+    torch.cuda.synchronize()
+    return d, layers, x, t_in, kvs, ws, x_out, t_out
+
+
+def cpu_baseline(c, cname, seconds_hint=20.0):
+    """The oracle (as it stands) on one decode layer for a few requests."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.threads()
+    h1, h2, heads = c["h1"], c["h2"], c["heads"]
+    D = h1 // heads
+    rb = max(1, min(16, threads))
+    T = c["s"] + c["n"] // 2                      # mean cache length over the decode steps
+    rng = np.random.default_rng(CONFIG_SEED[cname])
+    W = {}
+    for name, shp in (("wq", (h1, h1)), ("wk", (h1, h1)), ("wv", (h1, h1)), ("wo", (h1, h1)),
+                      ("w1", (h1, h2)), ("w2", (h2, h1))):
+        w = (rng.standard_normal(shp, dtype=np.float32) * 0.02).astype(np.float16)
+        if c["fmt"] == 1:
+            w = oracle.dequantize_g64(*oracle.quantize_g64(w))
+        W[name] = w
+    kv = oracle.KV(c["fmt"], rb, heads, T, D)
+    kx = rng.standard_normal((rb, heads, T - 1, D), dtype=np.float32).astype(np.float16)
+    vx = rng.standard_normal((rb, heads, T - 1, D), dtype=np.float32).astype(np.float16)
+    if c["fmt"] == 1:
+        kc, ks = oracle.quantize_g64(kx)
+        vc, vs = oracle.quantize_g64(vx)
+        kv.k[:, :, :T - 1], kv.ksm[:, :, :T - 1] = kc, ks
+        kv.v[:, :, :T - 1], kv.vsm[:, :, :T - 1] = vc, vs
+    else:
+        kv.k[:, :, :T - 1] = kx.view(np.uint16)
+        kv.v[:, :, :T - 1] = vx.view(np.uint16)
+    t = rng.standard_normal((rb, 1, h1), dtype=np.float32).astype(np.float16)
+    t0 = time.perf_counter()
+    oracle.layer_decode(t, W, kv, heads, T - 1)
+    dt = time.perf_counter() - t0
+    return {
+        "value": rb / (c["l"] * dt), "unit": "tokens/s", "cores": min(threads, rb),
+        "kind": "oracle",
+        "sample": f"one decode layer (of {c['l']}) for {rb} requests at cache length {T}, "
+                  f"{cname} shapes, fp64 sums; tokens/s = requests / (layers x layer time); "
+                  f"layer time {dt:.2f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="opt-175b-int4", choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; each GPU would run its own block "
+              "(data parallel, no exchange), so N > 1 is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_step_transformer_amd import hp
+
+    c = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    if hp.hp_device_check() != 0:
+        raise SystemExit(hp.hp_last_error())
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        log(f"setup {args.config}")
+        d, layers, x, t_in, kvs, ws, x_out, t_out = setup(c, CONFIG_SEED[args.config], hp, torch)
+        wbytes = sum(ly.nbytes() for ly in layers)
+        kvbytes = sum(kv.nbytes() for kv in kvs)
+        log(f"weights {wbytes / 1e9:.1f} GB, kv {kvbytes / 1e9:.1f} GB, ws {ws.numel() / 1e9:.1f} GB")
+
+        def block(timing):
+            return hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws, hp.HP_GRAPH,
+                                   timing=timing, stream=stream)
+
+        for i in range(args.warmup):
+            tw = block(True)
+            log(f"warmup {i}: prefill {tw[0]:.1f} ms decode {tw[1]:.1f} ms")
+        hp.hp_profile(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        times = []
+        for i in range(args.steps):
+            times.append(block(True))
+            log(f"step {i}: prefill {times[-1][0]:.1f} ms decode {times[-1][1]:.1f} ms")
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        hp.hp_profile(False)
+        prof = hp.hp_profile_read()
+
+        # decode-phase kernels: one eager decode column (cache rows already
+        # filled by the timed blocks), each launch timed with HIP events
+        T = c["s"] + c["n"] // 2
+        hp.hp_profile(True)
+        tcur = t_in[0].contiguous()
+        tnext = torch.empty_like(tcur)
+        for j in range(c["l"]):
+            hp.hp_layer_decode(d, layers[j], tcur, T - 1, 1, kvs[j], tnext, ws, stream=stream)
+            tcur, tnext = tnext, tcur
+        stream.synchronize()
+        hp.hp_profile(False)
+        dprof = hp.hp_profile_read()
+    nonfinite = int((~torch.isfinite(t_out.float())).sum().item())
+
+    b, n, s, l = c["b"], c["n"], c["s"], c["l"]
+    K = args.steps
+    pre_ms = sum(t[0] for t in times) / K
+    dec_ms = sum(t[1] for t in times) / K
+    value = b * n / (dec_ms / 1e3)
+
+    # dominant kernel of the timed region (by total event time)
+    dom = max(prof.items(), key=lambda kv: kv[1][1])
+    name, (launches, tot_ms) = dom
+    M = b * s
+    if name.startswith("gemm_") and name.endswith("_tiled"):
+        algo = K * l * layer_flops(c, M) / 1e12      # TFLOP over the timed region
+        achieved = algo / (tot_ms / 1e3)
+        roof = {"kernel": name, "bound": "mfma", "achieved": achieved,
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                "launches": launches, "avg_launch_ms": tot_ms / launches,
+                "work": "2*M*(4*h1^2 + 2*h1*h2) flops per layer, M = b*s"}
+    else:
+        roof = {"kernel": name, "bound": None, "achieved": None, "peak": None, "unit": None,
+                "frac": None, "traffic": None, "launches": launches,
+                "avg_launch_ms": tot_ms / launches}
+
+    # decode-phase kernels
+    dec = {}
+    for kname, (cnt, ms) in dprof.items():
+        e = {"launches": cnt, "avg_launch_ms": ms / cnt, "total_ms": ms}
+        if kname.startswith("gemm_") and kname.endswith("_skinny"):
+            fl = l * layer_flops(c, b) / 1e12
+            by = l * weight_bytes_per_layer(c) / 1e9
+            e.update(bound="mfma" if c["fmt"] == 1 else "hbm",
+                     tflops=fl / (ms / 1e3), gbs=by / (ms / 1e3))
+            e["frac_mfma"] = e["tflops"] / MFMA_F16_PEAK_TFLOPS
+            e["frac_hbm_weights"] = e["gbs"] / HBM_PEAK_GBS
+        if kname.startswith("attn_decode"):
+            by = l * kv_bytes_read(c, T) / 1e9
+            e.update(bound="hbm", gbs=by / (ms / 1e3), frac_hbm=by / (ms / 1e3) / HBM_PEAK_GBS)
+        dec[kname] = e
+
+    out = {
+        "metric": "generated tokens/s (b*n / decode time of the block)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config} block", "l": l, "h1": c["h1"], "h2": c["h2"],
+                   "heads": c["heads"], "b": b, "gbs": c["gbs"], "s": s, "n": n,
+                   "weights": "int4-g64" if c["fmt"] else "fp16",
+                   "kv": "int4-g64" if c["fmt"] else "fp16",
+                   "schedule": "zig-zag block, decode column as hipGraph"},
+        "prefill_ms": pre_ms,
+        "decode_ms": dec_ms,
+        "tokens_per_s_incl_prefill": b * n / ((pre_ms + dec_ms) / 1e3),
+        "resident_GB": {"weights": wbytes / 1e9, "kv": kvbytes / 1e9},
+        "nonfinite_decode_outputs": nonfinite,
+        "roofline": roof,
+        "decode_kernels": dec,
+        "kernels": {k: {"launches": v[0], "total_ms": v[1]} for k, v in prof.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(c, args.config)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

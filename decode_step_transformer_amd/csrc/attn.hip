@@ -414,6 +414,7 @@ void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const voi
   const int64_t groups = 2LL * b * q * heads * ((h1 / heads) / 64);
   if (groups == 0) return;
   const int blocks = (int)std::min<int64_t>(cdiv(groups, 32), 16384);
+  Prof prof(kv.fmt == HP_Q4 ? "kv_append_q4" : "kv_append_f16", st);
   if (kv.fmt == HP_Q4)
     hipLaunchKernelGGL(k_kv_append<true>, dim3(blocks), dim3(256), 0, st, a);
   else
@@ -428,6 +429,7 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
             (const uint32_t*)kv.v_sm, (_Float16*)out};
   const int D = h1 / heads;
   const dim3 grid((unsigned)((int64_t)b * heads * q));
+  Prof prof(kv.fmt == HP_Q4 ? "attn_decode_q4" : "attn_decode_f16", st);
   if (D == 128) {
     if (kv.fmt == HP_Q4)
       hipLaunchKernelGGL((k_decode_attn<128, true>), grid, dim3(64), 0, st, a);
@@ -445,6 +447,7 @@ void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, c
                               void* out, hipStream_t st) {
   const int D = h1 / heads;
   const dim3 grid((unsigned)((int64_t)b * heads * cdiv(s, 64)));
+  Prof prof("attn_prefill", st);
   if (D == 128)
     hipLaunchKernelGGL(k_prefill_attn<128>, grid, dim3(64), 0, st, (const _Float16*)qkv, s, h1,
                        heads, (_Float16*)out);
@@ -455,6 +458,7 @@ void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, c
 
 void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
                        hipStream_t st) {
+  Prof prof("tree_masks", st);
   hipLaunchKernelGGL(k_tree_masks, dim3(1), dim3(64), 0, st, b, q, parent, masks, err);
 }
 

@@ -18,6 +18,17 @@ hp_status launch_ok(const char* kernel);
 
 inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Per-kernel event timing (hp_profile): while enabled, a Prof object records
+// a start event on construction and a stop event on destruction, on the
+// launch stream, unless that stream is being captured into a graph.
+struct Prof {
+  Prof(const char* tag, hipStream_t st);
+  ~Prof();
+  const char* tag;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+};
+
 typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));

@@ -281,6 +281,9 @@ size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n) {
 
 template <int TM>
 static void launch_tm(const GemmArgs& a, bool q4, dim3 grid, hipStream_t st) {
+  const bool skinny = a.mtiles == 1 && TM <= 9 && a.M <= SKINNY_M;
+  Prof prof(q4 ? (skinny ? "gemm_q4_skinny" : "gemm_q4_tiled")
+               : (skinny ? "gemm_f16_skinny" : "gemm_f16_tiled"), st);
   if (q4)
     hipLaunchKernelGGL((k_gemm<TM, true>), grid, dim3(256), 0, st, a);
   else
@@ -330,6 +333,7 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
     if (s != HP_OK || splits == 1) return s;
     const int64_t quads = M * (w.n / 4);
     const int blocks = (int)std::min<int64_t>(cdiv(quads, 256), 8192);
+    Prof prof("gemm_splitk_reduce", st);
     hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, st, (const float*)ws, splits,
                        M, w.n, (const _Float16*)res, ldr, a.relu, (_Float16*)y, ldy);
     return launch_ok("k_splitk_reduce");

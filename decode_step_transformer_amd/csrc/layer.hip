@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <string>
 #include <vector>
 
 #include "common.h"
@@ -58,6 +59,7 @@ void launch_copy_step(const void* src, int64_t count_elems, int64_t stride_elems
                       const int32_t* dstep, void* dst, int direction, hipStream_t st) {
   const int64_t n16 = count_elems / 8;
   const int blocks = (int)std::min<int64_t>(cdiv(n16, 256), 4096);
+  Prof prof("copy_step", st);
   hipLaunchKernelGGL(k_copy_step, dim3(blocks), dim3(256), 0, st, (const uint4*)src, n16,
                      stride_elems / 8, dstep, (uint4*)dst, direction);
 }
@@ -234,6 +236,40 @@ static hp_kv kv_slice(const hp_kv& kv, int heads, int D, int64_t r0) {
     o.v_sm = (char*)kv.v_sm + rows * (D / 64) * 4;
   }
   return o;
+}
+
+// -------------------------------------------------------------- profiling
+static std::mutex g_pmu;
+static bool g_prof = false;
+static std::vector<std::pair<std::string, std::pair<hipEvent_t, hipEvent_t>>> g_prec;
+static std::vector<hipEvent_t> g_pool;
+
+static hipEvent_t pool_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+Prof::Prof(const char* t, hipStream_t s) : tag(t), st(s) {
+  if (!g_prof) return;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+  std::lock_guard<std::mutex> lk(g_pmu);
+  a = pool_event();
+  b = pool_event();
+  if (a && b) hipEventRecord(a, st);
+}
+
+Prof::~Prof() {
+  if (!a || !b) return;
+  hipEventRecord(b, st);
+  std::lock_guard<std::mutex> lk(g_pmu);
+  g_prec.push_back({tag, {a, b}});
 }
 
 // ----------------------------------------------------------------- graphs
@@ -605,6 +641,45 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   for (int i = 0; i < d->n; ++i)
     if ((s = hip_ok(hipGraphLaunch(exec, st), "hipGraphLaunch")) != HP_OK) return finish(s);
   return finish(HP_OK);
+}
+
+int32_t hp_profile(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_pmu);
+  if (on) {
+    for (auto& r : g_prec) {
+      g_pool.push_back(r.second.first);
+      g_pool.push_back(r.second.second);
+    }
+    g_prec.clear();
+  }
+  g_prof = on != 0;
+  return HP_OK;
+}
+
+int32_t hp_profile_read(char* buf, size_t len) {
+  std::lock_guard<std::mutex> lk(g_pmu);
+  std::map<std::string, std::pair<long, double>> agg;
+  for (auto& r : g_prec) {
+    hipError_t e = hipEventSynchronize(r.second.second);
+    if (e != hipSuccess) return hip_ok(e, "hipEventSynchronize");
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, r.second.first, r.second.second);
+    auto& a = agg[r.first];
+    a.first += 1;
+    a.second += ms;
+  }
+  std::string out;
+  char line[256];
+  for (auto& kv : agg) {
+    snprintf(line, sizeof(line), "%s %ld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    out += line;
+  }
+  if (buf && len) {
+    const size_t n = std::min(len - 1, out.size());
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  return (int32_t)agg.size();
 }
 
 void hp_release_graphs(void) {

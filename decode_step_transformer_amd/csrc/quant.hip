@@ -113,6 +113,7 @@ void launch_quantize_g64(const void* x, int64_t rows, int64_t cols, void* codes,
                          hipStream_t st) {
   const int64_t groups = rows * (cols / 64);
   if (groups == 0) return;
+  Prof prof("quantize_g64", st);
   hipLaunchKernelGGL(k_quantize_g64, dim3(grid_for(groups, 32)), dim3(256), 0, st,
                      (const uint4*)x, groups, (uint32_t*)codes, (uint32_t*)sm);
 }
@@ -121,6 +122,7 @@ void launch_dequantize_g64(const void* codes, const void* sm, int64_t rows, int6
                            hipStream_t st) {
   const int64_t words = rows * cols / 8;
   if (words == 0) return;
+  Prof prof("dequantize_g64", st);
   hipLaunchKernelGGL(k_dequantize_g64, dim3(grid_for(words, 256)), dim3(256), 0, st,
                      (const uint32_t*)codes, (const uint32_t*)sm, words, (uint4*)y);
 }

@@ -49,7 +49,7 @@ EXPORTS = [
     "hp_pack_weight_q4", "hp_pack_weight_f16", "hp_gemm_workspace_bytes", "hp_gemm",
     "hp_kv_append", "hp_prefill_attention", "hp_decode_attention", "hp_tree_masks",
     "hp_workspace_bytes", "hp_layer_prefill", "hp_layer_decode", "hp_run_block",
-    "hp_release_graphs", "hp_weight_bytes", "hp_kv_bytes",
+    "hp_release_graphs", "hp_weight_bytes", "hp_kv_bytes", "hp_profile", "hp_profile_read",
 ]
 
 _lib = None
@@ -95,6 +95,10 @@ def lib():
         L.hp_kv_bytes.argtypes = [C.POINTER(hp_dims), _i32]
         L.hp_kv_bytes.restype = C.c_uint64
         L.hp_release_graphs.restype = None
+        L.hp_profile.argtypes = [_i32]
+        L.hp_profile.restype = _i32
+        L.hp_profile_read.argtypes = [C.c_char_p, _sz]
+        L.hp_profile_read.restype = _i32
         _lib = L
     return _lib
 
@@ -321,3 +325,21 @@ def hp_weight_bytes(d: hp_dims, fmt: int) -> int:
 
 def hp_kv_bytes(d: hp_dims, fmt: int) -> int:
     return int(lib().hp_kv_bytes(C.byref(d), fmt))
+
+
+# ---------------------------------------------------------------- profiling
+def hp_profile(on: bool):
+    lib().hp_profile(1 if on else 0)
+
+
+def hp_profile_read() -> dict:
+    """{kernel: (launches, total_ms)} of the launches recorded since hp_profile(True)."""
+    buf = C.create_string_buffer(1 << 16)
+    n = lib().hp_profile_read(buf, len(buf))
+    if n < 0:
+        raise HPError(n, hp_last_error())
+    out = {}
+    for ln in buf.value.decode().splitlines():
+        name, cnt, ms = ln.split()
+        out[name] = (int(cnt), float(ms))
+    return out

@@ -242,6 +242,17 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
 /* Drops every captured graph (device memory of graph execs is released). */
 void hp_release_graphs(void);
 
+/* ------------------------------------------------------------ profiling */
+/* Diagnostics.  hp_profile(1) clears earlier records and makes every later
+ * kernel launch of the library record a start/stop HIP event pair on its own
+ * stream (launches inside a graph capture are not recorded); hp_profile(0)
+ * stops recording.  hp_profile_read() waits for the recorded events and
+ * writes one line "kernel launches total_ms" per kernel name into buf
+ * (NUL-terminated, truncated to len bytes); it returns the number of lines,
+ * or a negative hp_status. */
+int32_t hp_profile(int32_t on);
+int32_t hp_profile_read(char* buf, size_t len);
+
 /* ------------------------------------------------------------ sizes */
 /* [FlexGen] background section (memory bottleneck analysis): weight bytes
  * l(8 h1^2 + 4 h1 h2) in fp16, and peak KV bytes 4 b l h1 (s + n) in fp16;
