@@ -20,6 +20,8 @@
 //  * Skinny products (M <= 144, the decode step) split k over workgroups;
 //    partial sums go to fp32 scratch and a second kernel adds them in split
 //    order, so the result depends only on (k, n), never on M.
+#include <type_traits>
+
 #include "common.h"
 
 namespace hp {
@@ -28,24 +30,48 @@ constexpr int BK = 128;        // k-block (one packed q4 tile in depth)
 constexpr int LDS_ROW = 136;   // halves per staged activation row (128 + 8 pad)
 constexpr int SKINNY_M = 144;  // largest M handled as one row tile with split-k
 
-__device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
-// Expands one dword of 8 int4 codes (nibble order of the packed layout) to 8
-// binary16 values c * scale + min, given the 4 scale pairs and 4 min pairs.
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, uint4 s, uint4 m) {
-  const uint32_t sp[4] = {s.x, s.y, s.z, s.w};
-  const uint32_t mp[4] = {m.x, m.y, m.z, m.w};
-  const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
-  uint32_t out[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t u = ((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-    const f16x2 c = __builtin_bit_cast(f16x2, u) - off;  // exact small integers
-    const f16x2 y = __builtin_elementwise_fma(c, __builtin_bit_cast(f16x2, sp[p]),
-                                              __builtin_bit_cast(f16x2, mp[p]));
-    out[p] = __builtin_bit_cast(uint32_t, y);
+// Calls f(integral_constant<0>) .. f(integral_constant<N-1>): compile-time
+// indices, so register arrays indexed inside f stay in registers.
+template <int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (N > 0) {
+    unroll<N - 1>(f);
+    f(std::integral_constant<int, N - 1>());
   }
-  return as_f16x8(make_uint4(out[0], out[1], out[2], out[3]));
+}
+
+// Expands one dword of 8 int4 codes (nibble order of the packed layout:
+// pair p = (nibble p, nibble p+4) gives k-offsets (2p, 2p+1)) to 8 binary16
+// values c * scale + min, given the 4 scale pairs and 4 min pairs.
+// A nibble inserted at mantissa bits 0..3 of a half under the exponent of
+// 1024, or at bits 4..7 under the exponent of 64, has weight exactly 1, so
+// the half reads as magic + c and one packed subtraction gives the exact
+// integer c.  Pairs 0 and 1 sit at bits 0..3 and 4..7 of each half already;
+// pairs 2 and 3 after one shift by 8.  The final packed FMA rounds once, as
+// the dequantiser's definition requires.  Masks and magic patterns arrive in
+// registers so that each insert is one v_bfi_b32.
+struct DqConst {
+  uint32_t mask0, mask1;    // 0x000F000F, 0x00F000F0
+  uint32_t magic0, magic1;  // 0x64006400 (1024), 0x54005400 (64)
+};
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+__device__ __forceinline__ f16x2 fma2(f16x2 c, uint32_t s, uint32_t m) {
+  return __builtin_elementwise_fma(c, __builtin_bit_cast(f16x2, s), __builtin_bit_cast(f16x2, m));
+}
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, u32x4 s, u32x4 m, const DqConst& q) {
+  const f16x2 o0 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const f16x2 o1 = {(_Float16)64.0f, (_Float16)64.0f};
+  const uint32_t w8 = w >> 8;
+  const f16x2 c0 = __builtin_bit_cast(f16x2, bfi(q.mask0, w, q.magic0)) - o0;
+  const f16x2 c1 = __builtin_bit_cast(f16x2, bfi(q.mask1, w, q.magic1)) - o1;
+  const f16x2 c2 = __builtin_bit_cast(f16x2, bfi(q.mask0, w8, q.magic0)) - o0;
+  const f16x2 c3 = __builtin_bit_cast(f16x2, bfi(q.mask1, w8, q.magic1)) - o1;
+  return as_f16x8(u32x4{__builtin_bit_cast(uint32_t, fma2(c0, s[0], m[0])),
+                        __builtin_bit_cast(uint32_t, fma2(c1, s[1], m[1])),
+                        __builtin_bit_cast(uint32_t, fma2(c2, s[2], m[2])),
+                        __builtin_bit_cast(uint32_t, fma2(c3, s[3], m[3]))});
 }
 
 struct GemmArgs {
@@ -57,6 +83,7 @@ struct GemmArgs {
   int K, N, kb_per_split, mtiles;
   const _Float16* res;
   int64_t ldr;
+  DqConst dq;
   int relu;
   _Float16* Y;
   int64_t ldy;
@@ -66,7 +93,11 @@ struct GemmArgs {
 template <int TM, bool Q4>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   constexpr int BM = 16 * TM;
+  constexpr int NBUF = Q4 ? 3 : 2;  // weight k-blocks in flight in registers
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDS_ROW];
+  // per-wave int4 group scales/mins of one k-block (128 k): 64 dwords of
+  // scale pairs, then 64 dwords of min pairs; two stages
+  __shared__ __attribute__((aligned(16))) uint32_t Ssm[Q4 ? 4 : 1][2][128];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KB = g.K / BK;
@@ -89,115 +120,191 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const int64_t m0 = (int64_t)mt * BM;
   const int n_wave = nt * 256 + wave * 64;
   const bool wave_on = n_wave < g.N;
+  // a wave past the last column reloads the last group (never stored), so
+  // every load is unconditional and wait counts stay static
+  const int n_ld = min(n_wave, g.N - 64);
   const int split = blockIdx.y;
   const int kb0 = split * g.kb_per_split, kb1 = kb0 + g.kb_per_split;
 
-  // ---- activation tile loader: TM 16-byte chunks per thread ----
-  uint4 areg[TM];
-  auto load_a = [&](int kb) {
-#pragma unroll
-    for (int c = 0; c < TM; ++c) {
-      const int chunk = tid + 256 * c;
-      const int row = chunk >> 4, col = (chunk & 15) * 8;
-      const int64_t m = m0 + row;
-      areg[c] = (m < g.M) ? *(const uint4*)(g.A + m * g.lda + (int64_t)kb * BK + col)
-                          : make_uint4(0, 0, 0, 0);
-    }
+  // ---- activation tile loader: TM 16-byte chunks per thread.  Rows past M
+  // reload row M-1 (their outputs are never stored).
+  u32x4 areg[TM];
+  // chunk c of this thread: row (tid >> 4) + 16 c, column (tid & 15) * 8
+  const _Float16* abase = g.A + (int64_t)((tid & 15) * 8);
+  const int64_t arow0 = m0 + (tid >> 4);
+  auto load_a = [&](int kb) __attribute__((always_inline)) {
+    unroll<TM>([&](auto c_) {
+      constexpr int c = decltype(c_)::value;
+      const int64_t m = min(arow0 + 16 * c, g.M - 1);
+      areg[c] = *(const u32x4*)(abase + m * g.lda + (int64_t)kb * BK);
+    });
   };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < TM; ++c) {
+  auto store_a = [&](int buf) __attribute__((always_inline)) {
+    unroll<TM>([&](auto c_) {
+      constexpr int c = decltype(c_)::value;
       const int chunk = tid + 256 * c;
-      const int row = chunk >> 4, col = (chunk & 15) * 8;
-      *(uint4*)(&As[buf][row * LDS_ROW + col]) = areg[c];
-    }
+      *(u32x4*)(&As[buf][(chunk >> 4) * LDS_ROW + (chunk & 15) * 8]) = areg[c];
+    });
   };
 
-  // ---- weight fragment loader (double-buffered in registers) ----
+  // ---- weight fragments ----
   const int kq = lane >> 4, r16 = lane & 15;
-  const int grp = n_wave >> 6;
   struct Raw {
-    uint4 c[Q4 ? 4 : 16];  // Q4: codes per subtile; F16: 4 chunks per subtile
-    uint4 sc[Q4 ? 4 : 1], mn[Q4 ? 4 : 1];
+    u32x4 c[Q4 ? 4 : 16];  // Q4: codes per subtile; F16: 4 chunks per subtile
   };
-  auto load_b = [&](Raw& R, int kb) {
-    if (!wave_on) return;
+  const u32x4* Bq = (const u32x4*)g.B + ((int64_t)(n_ld >> 4) * KB) * 64 + lane;
+  const _Float16* Bh = (const _Float16*)g.B + (int64_t)(n_ld + r16) * g.K + 32 * kq;
+  auto load_b = [&](Raw& R, int kb) __attribute__((always_inline)) {
     if constexpr (Q4) {
-      const uint4* P = (const uint4*)g.B;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) R.c[t] = P[((int64_t)((n_wave >> 4) + t) * KB + kb) * 64 + lane];
-      const int64_t so = (int64_t)grp * g.K + (int64_t)kb * BK + 32 * kq;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        R.sc[j] = *(const uint4*)(g.scale + so + 8 * j);
-        R.mn[j] = *(const uint4*)(g.minv + so + 8 * j);
-      }
+      unroll<4>([&](auto t_) {
+        constexpr int t = decltype(t_)::value;
+        R.c[t] = Bq[((int64_t)t * KB + kb) * 64];
+      });
     } else {
-      const _Float16* W = (const _Float16*)g.B;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint4* p = (const uint4*)(W + (int64_t)(n_wave + 16 * t + r16) * g.K +
-                                        (int64_t)kb * BK + 32 * kq);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) R.c[4 * t + j] = p[j];
-      }
+      unroll<4>([&](auto t_) {
+        constexpr int t = decltype(t_)::value;
+        const u32x4* p = (const u32x4*)(Bh + (int64_t)16 * t * g.K + (int64_t)kb * BK);
+        unroll<4>([&](auto j_) {
+          constexpr int j = decltype(j_)::value;
+          R.c[4 * t + j] = p[j];
+        });
+      });
     }
+  };
+  // scale/min of this wave's group for one k-block: lanes 0-31 fetch scale
+  // pairs, lanes 32-63 min pairs, 8 bytes each
+  const _Float16* smsrc = (lane < 32 ? g.scale : g.minv) + (int64_t)(n_ld >> 6) * g.K + 4 * (lane & 31);
+  u32x2 sreg;
+  auto load_sm = [&](int kb) __attribute__((always_inline)) {
+    if constexpr (Q4) sreg = *(const u32x2*)(smsrc + (int64_t)kb * BK);
+  };
+  auto store_sm = [&](int stage) __attribute__((always_inline)) {
+    if constexpr (Q4) *(u32x2*)&Ssm[wave][stage][2 * lane] = sreg;
   };
 
   f32x4 acc[TM][4];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unroll<TM>([&](auto i_) {
+    unroll<4>([&](auto t_) { acc[decltype(i_)::value][decltype(t_)::value] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+  });
 
-  auto compute = [&](const Raw& R, int cur) {
-    if (!wave_on) return;
-    const _Float16* Ab = &As[cur][0];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f16x8 wf[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
+  // Multiplies k-block kb (activation buffer `cur`, weight registers R).
+  // Software pipeline over the 4 MFMA k-steps j: while the MFMAs of step j
+  // run, the LDS fragments of step j+1 are read and its weights dequantised.
+  auto compute = [&](const Raw& R, int cur, int stage) __attribute__((always_inline)) {
+    const _Float16* Ab = &As[cur][0] + r16 * LDS_ROW + 32 * kq;
+    const uint32_t* Sb = &Ssm[Q4 ? wave : 0][stage][16 * kq];
+    f16x8 xa[TM], xb[TM], wa[4], wb[4];
+    u32x4 sa, ma, sb, mb;
+    auto read_x = [&](f16x8 (&x)[TM], int j) __attribute__((always_inline)) {
+      unroll<TM>([&](auto i_) {
+        constexpr int i = decltype(i_)::value;
+        x[i] = *(const f16x8*)(Ab + 16 * i * LDS_ROW + 8 * j);
+      });
+    };
+    auto read_s = [&](u32x4& sv, u32x4& mv, int j) __attribute__((always_inline)) {
+      if constexpr (Q4) {
+        sv = *(const u32x4*)(Sb + 4 * j);
+        mv = *(const u32x4*)(Sb + 64 + 4 * j);
+      }
+    };
+    auto make_w = [&](f16x8 (&w)[4], const u32x4& sv, const u32x4& mv, auto j_) __attribute__((always_inline)) {
+      constexpr int j = decltype(j_)::value;
+      unroll<4>([&](auto t_) {
+        constexpr int t = decltype(t_)::value;
         if constexpr (Q4) {
-          const uint4 c = R.c[t];
-          const uint32_t w = j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
-          wf[t] = dequant8(w, R.sc[j], R.mn[j]);
+          w[t] = dequant8(R.c[t][j], sv, mv, g.dq);
         } else {
-          wf[t] = as_f16x8(R.c[4 * t + j]);
+          w[t] = as_f16x8(R.c[4 * t + j]);
         }
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const f16x8 xf = *(const f16x8*)(Ab + (16 * i + r16) * LDS_ROW + 32 * kq + 8 * j);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[t], xf, acc[i][t], 0, 0, 0);
-      }
-    }
+      });
+    };
+    auto mma = [&](const f16x8 (&w)[4], const f16x8 (&x)[TM]) __attribute__((always_inline)) {
+      unroll<TM>([&](auto i_) {
+        constexpr int i = decltype(i_)::value;
+        unroll<4>([&](auto t_) {
+          constexpr int t = decltype(t_)::value;
+          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[t], x[i], acc[i][t], 0, 0, 0);
+        });
+      });
+    };
+    // issue order for one j-step: the LDS reads of the next step first, then
+    // each MFMA followed by two VALU instructions (the next step's dequant)
+    auto interleave = [&]() __attribute__((always_inline)) {
+      unroll<TM + 2>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+      unroll<4 * TM>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      });
+    };
+    read_s(sa, ma, 0);
+    read_x(xa, 0);
+    make_w(wa, sa, ma, std::integral_constant<int, 0>());
+    __builtin_amdgcn_sched_barrier(0);
+    read_s(sb, mb, 1);
+    read_x(xb, 1);
+    mma(wa, xa);
+    make_w(wb, sb, mb, std::integral_constant<int, 1>());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    read_s(sa, ma, 2);
+    read_x(xa, 2);
+    mma(wb, xb);
+    make_w(wa, sa, ma, std::integral_constant<int, 2>());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    read_s(sb, mb, 3);
+    read_x(xb, 3);
+    mma(wa, xa);
+    make_w(wb, sb, mb, std::integral_constant<int, 3>());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    mma(wb, xb);
   };
 
-  // one k-block: prefetch the next activation tile and weight fragments,
-  // multiply this block, then publish the next activation tile
-  auto step = [&](int kb, const Raw& cur_b, Raw& next_b) {
-    const int cur = (kb - kb0) & 1;
-    const bool more = kb + 1 < kb1;
-    if (more) {
-      load_a(kb + 1);
-      load_b(next_b, kb + 1);
-    }
-    compute(cur_b, cur);
-    if (more) store_a(cur ^ 1);
+  Raw r0, r1, r2;
+  // prologue: activation block kb0 and scales of kb0 into LDS; weight
+  // registers for the first NBUF-1 blocks
+  load_sm(kb0);
+  load_a(kb0);
+  load_b(r0, kb0);
+  if constexpr (NBUF > 2) load_b(r1, min(kb0 + 1, kb1 - 1));
+  store_a(0);
+  store_sm(0);
+  __syncthreads();
+
+  // one k-block kb (weights in `cur`): prefetch the scales and activation
+  // block of kb+1 (stored to LDS at the end) and the weights of kb+NBUF-1
+  // (into `fill`), then multiply kb.  Past the end, indices clamp to the last
+  // block: the extra loads are discarded.
+  auto step = [&](const Raw& cur, Raw& fill, int kb) __attribute__((always_inline)) {
+    const int nx = min(kb + 1, kb1 - 1);
+    load_sm(nx);
+    load_a(nx);
+    load_b(fill, min(kb + NBUF - 1, kb1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, (kb - kb0) & 1, (kb - kb0) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(((kb - kb0) & 1) ^ 1);
+    store_sm(((kb - kb0) & 1) ^ 1);
     __syncthreads();
   };
-
-  Raw b0, b1;
-  load_a(kb0);
-  store_a(0);
-  load_b(b0, kb0);
-  __syncthreads();
-  for (int kb = kb0; kb < kb1; kb += 2) {
-    step(kb, b0, b1);
-    if (kb + 1 < kb1) step(kb + 1, b1, b0);
+  // whole rounds of NBUF steps, then the remainder: no branch inside the
+  // loop body, so the accumulators never pass through a join
+  int kb = kb0;
+  if constexpr (NBUF == 3) {
+    for (; kb + 3 <= kb1; kb += 3) {
+      step(r0, r2, kb);
+      step(r1, r0, kb + 1);
+      step(r2, r1, kb + 2);
+    }
+    if (kb < kb1) step(r0, r2, kb);
+    if (kb + 1 < kb1) step(r1, r0, kb + 1);
+  } else {
+    for (; kb + 2 <= kb1; kb += 2) {
+      step(r0, r1, kb);
+      step(r1, r0, kb + 1);
+    }
+    if (kb < kb1) step(r0, r1, kb);
   }
 
   if (!wave_on) return;
@@ -308,6 +415,7 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
   a.Y = (_Float16*)y;
   a.ldy = ldy;
   a.P = nullptr;
+  a.dq = DqConst{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
   const bool q4 = w.fmt == HP_Q4;
   const int KB = w.k / BK;
   const int ntiles = (int)cdiv(w.n, 256);
