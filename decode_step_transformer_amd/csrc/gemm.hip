@@ -51,12 +51,19 @@ __device__ __forceinline__ void unroll(F&& f) {
 // integer c.  Pairs 0 and 1 sit at bits 0..3 and 4..7 of each half already;
 // pairs 2 and 3 after one shift by 8.  The final packed FMA rounds once, as
 // the dequantiser's definition requires.  Masks and magic patterns arrive in
-// registers so that each insert is one v_bfi_b32.
+// registers so that each insert is one v_and_or_b32.
 struct DqConst {
   uint32_t mask0, mask1;    // 0x000F000F, 0x00F000F0
   uint32_t magic0, magic1;  // 0x64006400 (1024), 0x54005400 (64)
 };
-__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+// (a & m) | b with b & m == 0: one v_and_or_b32 (m in an SGPR, b in a VGPR:
+// a VOP3 instruction may read only one SGPR)
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | b; }
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(x));
+  return r;
+}
 __device__ __forceinline__ f16x2 fma2(f16x2 c, uint32_t s, uint32_t m) {
   return __builtin_elementwise_fma(c, __builtin_bit_cast(f16x2, s), __builtin_bit_cast(f16x2, m));
 }
@@ -91,13 +98,13 @@ struct GemmArgs {
 };
 
 template <int TM, bool Q4>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
+__global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
   constexpr int BM = 16 * TM;
-  constexpr int NBUF = Q4 ? 3 : 2;  // weight k-blocks in flight in registers
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDS_ROW];
+  constexpr int NS = 3;  // LDS stages (activations, scales) and weight register slots
+  __shared__ __attribute__((aligned(16))) _Float16 As[NS][BM * LDS_ROW];
   // per-wave int4 group scales/mins of one k-block (128 k): 64 dwords of
-  // scale pairs, then 64 dwords of min pairs; two stages
-  __shared__ __attribute__((aligned(16))) uint32_t Ssm[Q4 ? 4 : 1][2][128];
+  // scale pairs, then 64 dwords of min pairs
+  __shared__ __attribute__((aligned(16))) uint32_t Ssm[Q4 ? 4 : 1][NS][128];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int KB = g.K / BK;
@@ -125,6 +132,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const int n_ld = min(n_wave, g.N - 64);
   const int split = blockIdx.y;
   const int kb0 = split * g.kb_per_split, kb1 = kb0 + g.kb_per_split;
+  auto clampk = [&](int kb) __attribute__((always_inline)) { return min(kb, kb1 - 1); };
 
   // ---- activation tile loader: TM 16-byte chunks per thread.  Rows past M
   // reload row M-1 (their outputs are never stored).
@@ -139,11 +147,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       areg[c] = *(const u32x4*)(abase + m * g.lda + (int64_t)kb * BK);
     });
   };
-  auto store_a = [&](int buf) __attribute__((always_inline)) {
+  auto store_a = [&](int stage) __attribute__((always_inline)) {
     unroll<TM>([&](auto c_) {
       constexpr int c = decltype(c_)::value;
       const int chunk = tid + 256 * c;
-      *(u32x4*)(&As[buf][(chunk >> 4) * LDS_ROW + (chunk & 15) * 8]) = areg[c];
+      *(u32x4*)(&As[stage][(chunk >> 4) * LDS_ROW + (chunk & 15) * 8]) = areg[c];
     });
   };
 
@@ -182,130 +190,118 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     if constexpr (Q4) *(u32x2*)&Ssm[wave][stage][2 * lane] = sreg;
   };
 
+  const DqConst dq{g.dq.mask0, g.dq.mask1, in_vgpr(g.dq.magic0), in_vgpr(g.dq.magic1)};
   f32x4 acc[TM][4];
   unroll<TM>([&](auto i_) {
     unroll<4>([&](auto t_) { acc[decltype(i_)::value][decltype(t_)::value] = f32x4{0.f, 0.f, 0.f, 0.f}; });
   });
 
-  // Multiplies k-block kb (activation buffer `cur`, weight registers R).
-  // Software pipeline over the 4 MFMA k-steps j: while the MFMAs of step j
-  // run, the LDS fragments of step j+1 are read and its weights dequantised.
-  auto compute = [&](const Raw& R, int cur, int stage) __attribute__((always_inline)) {
-    const _Float16* Ab = &As[cur][0] + r16 * LDS_ROW + 32 * kq;
-    const uint32_t* Sb = &Ssm[Q4 ? wave : 0][stage][16 * kq];
-    f16x8 xa[TM], xb[TM], wa[4], wb[4];
-    u32x4 sa, ma, sb, mb;
-    auto read_x = [&](f16x8 (&x)[TM], int j) __attribute__((always_inline)) {
-      unroll<TM>([&](auto i_) {
-        constexpr int i = decltype(i_)::value;
-        x[i] = *(const f16x8*)(Ab + 16 * i * LDS_ROW + 8 * j);
-      });
-    };
-    auto read_s = [&](u32x4& sv, u32x4& mv, int j) __attribute__((always_inline)) {
-      if constexpr (Q4) {
-        sv = *(const u32x4*)(Sb + 4 * j);
-        mv = *(const u32x4*)(Sb + 64 + 4 * j);
-      }
-    };
-    auto make_w = [&](f16x8 (&w)[4], const u32x4& sv, const u32x4& mv, auto j_) __attribute__((always_inline)) {
-      constexpr int j = decltype(j_)::value;
+  // ---- one MFMA k-step (32 deep): fragments of (stage, j) ----
+  f16x8 xa[TM], xb[TM], wa[4], wb[4];
+  auto read_x = [&](f16x8 (&x)[TM], int stage, int j) __attribute__((always_inline)) {
+    const _Float16* Ab = &As[stage][0] + r16 * LDS_ROW + 32 * kq + 8 * j;
+    unroll<TM>([&](auto i_) {
+      constexpr int i = decltype(i_)::value;
+      x[i] = *(const f16x8*)(Ab + 16 * i * LDS_ROW);
+    });
+  };
+  auto make_w = [&](f16x8 (&w)[4], const Raw& R, int stage, auto j_) __attribute__((always_inline)) {
+    constexpr int j = decltype(j_)::value;
+    if constexpr (Q4) {
+      const uint32_t* Sb = &Ssm[wave][stage][16 * kq + 4 * j];
+      const u32x4 sv = *(const u32x4*)Sb;
+      const u32x4 mv = *(const u32x4*)(Sb + 64);
       unroll<4>([&](auto t_) {
         constexpr int t = decltype(t_)::value;
-        if constexpr (Q4) {
-          w[t] = dequant8(R.c[t][j], sv, mv, g.dq);
-        } else {
-          w[t] = as_f16x8(R.c[4 * t + j]);
-        }
+        w[t] = dequant8(R.c[t][j], sv, mv, dq);
       });
-    };
-    auto mma = [&](const f16x8 (&w)[4], const f16x8 (&x)[TM]) __attribute__((always_inline)) {
-      unroll<TM>([&](auto i_) {
-        constexpr int i = decltype(i_)::value;
-        unroll<4>([&](auto t_) {
-          constexpr int t = decltype(t_)::value;
-          acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[t], x[i], acc[i][t], 0, 0, 0);
-        });
+    } else {
+      unroll<4>([&](auto t_) {
+        constexpr int t = decltype(t_)::value;
+        w[t] = as_f16x8(R.c[4 * t + j]);
       });
-    };
-    // issue order for one j-step: the LDS reads of the next step first, then
-    // each MFMA followed by two VALU instructions (the next step's dequant)
-    auto interleave = [&]() __attribute__((always_inline)) {
-      unroll<TM + 2>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
-      unroll<4 * TM>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+  };
+  auto mma = [&](const f16x8 (&w)[4], const f16x8 (&x)[TM]) __attribute__((always_inline)) {
+    unroll<TM>([&](auto i_) {
+      constexpr int i = decltype(i_)::value;
+      unroll<4>([&](auto t_) {
+        constexpr int t = decltype(t_)::value;
+        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[t], x[i], acc[i][t], 0, 0, 0);
       });
-    };
-    read_s(sa, ma, 0);
-    read_x(xa, 0);
-    make_w(wa, sa, ma, std::integral_constant<int, 0>());
-    __builtin_amdgcn_sched_barrier(0);
-    read_s(sb, mb, 1);
-    read_x(xb, 1);
-    mma(wa, xa);
-    make_w(wb, sb, mb, std::integral_constant<int, 1>());
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    read_s(sa, ma, 2);
-    read_x(xa, 2);
-    mma(wb, xb);
-    make_w(wa, sa, ma, std::integral_constant<int, 2>());
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    read_s(sb, mb, 3);
-    read_x(xb, 3);
-    mma(wa, xa);
-    make_w(wb, sb, mb, std::integral_constant<int, 3>());
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    mma(wb, xb);
+    });
+  };
+  // issue order inside one k-step: the LDS reads of the next step first,
+  // then each MFMA followed by two VALU instructions (the next dequant)
+  auto interleave = [&]() __attribute__((always_inline)) {
+    unroll<TM + 2>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+    unroll<4 * TM>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    });
   };
 
   Raw r0, r1, r2;
-  // prologue: activation block kb0 and scales of kb0 into LDS; weight
-  // registers for the first NBUF-1 blocks
-  load_sm(kb0);
+  // prologue: stages 0 and 1 hold activation/scale blocks kb0 and kb0+1;
+  // weight slots 0 and 1 hold kb0 and kb0+1; registers hold block kb0+2
   load_a(kb0);
+  load_sm(kb0);
   load_b(r0, kb0);
-  if constexpr (NBUF > 2) load_b(r1, min(kb0 + 1, kb1 - 1));
+  load_b(r1, clampk(kb0 + 1));
   store_a(0);
   store_sm(0);
+  load_a(clampk(kb0 + 1));
+  load_sm(clampk(kb0 + 1));
+  store_a(1);
+  store_sm(1);
+  load_a(clampk(kb0 + 2));
+  load_sm(clampk(kb0 + 2));
   __syncthreads();
+  read_x(xa, 0, 0);
+  make_w(wa, r0, 0, std::integral_constant<int, 0>());
 
-  // one k-block kb (weights in `cur`): prefetch the scales and activation
-  // block of kb+1 (stored to LDS at the end) and the weights of kb+NBUF-1
-  // (into `fill`), then multiply kb.  Past the end, indices clamp to the last
-  // block: the extra loads are discarded.
-  auto step = [&](const Raw& cur, Raw& fill, int kb) __attribute__((always_inline)) {
-    const int nx = min(kb + 1, kb1 - 1);
-    load_sm(nx);
-    load_a(nx);
-    load_b(fill, min(kb + NBUF - 1, kb1 - 1));
+  // k-block kb in stage st % 3, weights in `cur`; `nxt` holds kb+1, `fill`
+  // receives kb+2.  At entry xa/wa hold the fragments of (kb, j = 0).
+  auto step = [&](const Raw& cur, const Raw& nxt, Raw& fill, int kb) __attribute__((always_inline)) {
+    const int st = (kb - kb0) % NS, st1 = (kb - kb0 + 1) % NS, st2 = (kb - kb0 + 2) % NS;
+    __syncthreads();  // every wave is done with stage st2 (block kb-1)
+    store_a(st2);
+    store_sm(st2);
+    load_a(clampk(kb + 3));
+    load_sm(clampk(kb + 3));
+    load_b(fill, clampk(kb + 2));
     __builtin_amdgcn_sched_barrier(0);
-    compute(cur, (kb - kb0) & 1, (kb - kb0) & 1);
+    read_x(xb, st, 1);
+    mma(wa, xa);
+    make_w(wb, cur, st, std::integral_constant<int, 1>());
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
-    store_a(((kb - kb0) & 1) ^ 1);
-    store_sm(((kb - kb0) & 1) ^ 1);
-    __syncthreads();
+    read_x(xa, st, 2);
+    mma(wb, xb);
+    make_w(wa, cur, st, std::integral_constant<int, 2>());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    read_x(xb, st, 3);
+    mma(wa, xa);
+    make_w(wb, cur, st, std::integral_constant<int, 3>());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    read_x(xa, st1, 0);
+    mma(wb, xb);
+    make_w(wa, nxt, st1, std::integral_constant<int, 0>());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // whole rounds of NBUF steps, then the remainder: no branch inside the
-  // loop body, so the accumulators never pass through a join
+  // whole rounds of 3 steps, then the remainder: no branch inside the loop
+  // body, so the accumulators never pass through a join
   int kb = kb0;
-  if constexpr (NBUF == 3) {
-    for (; kb + 3 <= kb1; kb += 3) {
-      step(r0, r2, kb);
-      step(r1, r0, kb + 1);
-      step(r2, r1, kb + 2);
-    }
-    if (kb < kb1) step(r0, r2, kb);
-    if (kb + 1 < kb1) step(r1, r0, kb + 1);
-  } else {
-    for (; kb + 2 <= kb1; kb += 2) {
-      step(r0, r1, kb);
-      step(r1, r0, kb + 1);
-    }
-    if (kb < kb1) step(r0, r1, kb);
+  for (; kb + 3 <= kb1; kb += 3) {
+    step(r0, r1, r2, kb);
+    step(r1, r2, r0, kb + 1);
+    step(r2, r0, r1, kb + 2);
   }
+  if (kb < kb1) step(r0, r1, r2, kb);
+  if (kb + 1 < kb1) step(r1, r2, r0, kb + 1);
 
   if (!wave_on) return;
   // ---- epilogue: lane holds rows m = m0 + 16 i + r16, columns n .. n+3 ----
@@ -388,7 +384,7 @@ size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n) {
 
 template <int TM>
 static void launch_tm(const GemmArgs& a, bool q4, dim3 grid, hipStream_t st) {
-  const bool skinny = a.mtiles == 1 && TM <= 9 && a.M <= SKINNY_M;
+  const bool skinny = a.mtiles == 1 && a.M <= SKINNY_M;
   Prof prof(q4 ? (skinny ? "gemm_q4_skinny" : "gemm_q4_tiled")
                : (skinny ? "gemm_f16_skinny" : "gemm_f16_tiled"), st);
   if (q4)
@@ -447,9 +443,15 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
     return launch_ok("k_splitk_reduce");
   }
   a.kb_per_split = KB;
-  a.mtiles = (int)cdiv(M, 128);
-  const dim3 grid((unsigned)(a.mtiles * ntiles), 1);
-  launch_tm<8>(a, q4, grid, st);
+  if (q4) {
+    // 64-row tiles at two workgroups per CU: two waves per SIMD keep the
+    // matrix pipe fed (one wave alone cannot issue MFMAs back to back)
+    a.mtiles = (int)cdiv(M, 64);
+    launch_tm<4>(a, q4, dim3((unsigned)(a.mtiles * ntiles), 1), st);
+  } else {
+    a.mtiles = (int)cdiv(M, 128);
+    launch_tm<8>(a, q4, dim3((unsigned)(a.mtiles * ntiles), 1), st);
+  }
   return launch_ok("k_gemm");
 }
 
