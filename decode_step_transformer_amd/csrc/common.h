@@ -51,9 +51,16 @@ void launch_pack_q4(const void* codes, const void* sm, int32_t k, int32_t n, voi
 void launch_pack_f16(const void* w, int32_t k, int32_t n, void* wt, hipStream_t st);
 
 // GEMM: y = act(x·w) + res (see hp_gemm).  ws holds split-K partials.
-size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n);
+size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt);
 hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, const void* res,
                       int64_t ldr, bool relu, void* y, int64_t ldy, void* ws, hipStream_t st);
+
+// fp16 tiled product for tall M (wt = [n][k] fp16) and the int4 -> fp16
+// weight expansion that feeds it.
+hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int k, int n, int64_t M,
+                        const void* res, int64_t ldr, bool relu, void* y, int64_t ldy,
+                        hipStream_t st);
+hp_status launch_expand_q4(const hp_mat& w, void* wt, hipStream_t st);
 
 // KV append / attention.  `dpos` (device int32, may be NULL): when set, the
 // kernels read pos from it (plus pos as an offset), so a captured graph can

@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dequant_dev.h"
 
 namespace hp {
 
@@ -30,7 +31,6 @@ constexpr int BK = 128;        // k-block (one packed q4 tile in depth)
 constexpr int LDS_ROW = 136;   // halves per staged activation row (128 + 8 pad)
 constexpr int SKINNY_M = 144;  // largest M handled as one row tile with split-k
 
-__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 // Calls f(integral_constant<0>) .. f(integral_constant<N-1>): compile-time
 // indices, so register arrays indexed inside f stay in registers.
@@ -40,45 +40,6 @@ __device__ __forceinline__ void unroll(F&& f) {
     unroll<N - 1>(f);
     f(std::integral_constant<int, N - 1>());
   }
-}
-
-// Expands one dword of 8 int4 codes (nibble order of the packed layout:
-// pair p = (nibble p, nibble p+4) gives k-offsets (2p, 2p+1)) to 8 binary16
-// values c * scale + min, given the 4 scale pairs and 4 min pairs.
-// A nibble inserted at mantissa bits 0..3 of a half under the exponent of
-// 1024, or at bits 4..7 under the exponent of 64, has weight exactly 1, so
-// the half reads as magic + c and one packed subtraction gives the exact
-// integer c.  Pairs 0 and 1 sit at bits 0..3 and 4..7 of each half already;
-// pairs 2 and 3 after one shift by 8.  The final packed FMA rounds once, as
-// the dequantiser's definition requires.  Masks and magic patterns arrive in
-// registers so that each insert is one v_and_or_b32.
-struct DqConst {
-  uint32_t mask0, mask1;    // 0x000F000F, 0x00F000F0
-  uint32_t magic0, magic1;  // 0x64006400 (1024), 0x54005400 (64)
-};
-// (a & m) | b with b & m == 0: one v_and_or_b32 (m in an SGPR, b in a VGPR:
-// a VOP3 instruction may read only one SGPR)
-__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | b; }
-__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(x));
-  return r;
-}
-__device__ __forceinline__ f16x2 fma2(f16x2 c, uint32_t s, uint32_t m) {
-  return __builtin_elementwise_fma(c, __builtin_bit_cast(f16x2, s), __builtin_bit_cast(f16x2, m));
-}
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, u32x4 s, u32x4 m, const DqConst& q) {
-  const f16x2 o0 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const f16x2 o1 = {(_Float16)64.0f, (_Float16)64.0f};
-  const uint32_t w8 = w >> 8;
-  const f16x2 c0 = __builtin_bit_cast(f16x2, bfi(q.mask0, w, q.magic0)) - o0;
-  const f16x2 c1 = __builtin_bit_cast(f16x2, bfi(q.mask1, w, q.magic1)) - o1;
-  const f16x2 c2 = __builtin_bit_cast(f16x2, bfi(q.mask0, w8, q.magic0)) - o0;
-  const f16x2 c3 = __builtin_bit_cast(f16x2, bfi(q.mask1, w8, q.magic1)) - o1;
-  return as_f16x8(u32x4{__builtin_bit_cast(uint32_t, fma2(c0, s[0], m[0])),
-                        __builtin_bit_cast(uint32_t, fma2(c1, s[1], m[1])),
-                        __builtin_bit_cast(uint32_t, fma2(c2, s[2], m[2])),
-                        __builtin_bit_cast(uint32_t, fma2(c3, s[3], m[3]))});
 }
 
 struct GemmArgs {
@@ -376,8 +337,9 @@ static int split_for(int32_t k, int32_t n) {
   return best;
 }
 
-size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n) {
-  if (M > SKINNY_M || M <= 0) return 0;
+size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {
+  if (M <= 0) return 0;
+  if (M > SKINNY_M) return fmt == HP_Q4 ? (size_t)k * (size_t)n * 2 : 0;  // fp16 expansion
   const int s = split_for(k, n);
   return s > 1 ? (size_t)s * (size_t)M * (size_t)n * sizeof(float) : 0;
 }
@@ -442,17 +404,14 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
                        M, w.n, (const _Float16*)res, ldr, a.relu, (_Float16*)y, ldy);
     return launch_ok("k_splitk_reduce");
   }
-  a.kb_per_split = KB;
+  // tall products: fp16 MFMA kernel over LDS tiles; int4 weights are first
+  // expanded to fp16 into the scratch buffer
   if (q4) {
-    // 64-row tiles at two workgroups per CU: two waves per SIMD keep the
-    // matrix pipe fed (one wave alone cannot issue MFMAs back to back)
-    a.mtiles = (int)cdiv(M, 64);
-    launch_tm<4>(a, q4, dim3((unsigned)(a.mtiles * ntiles), 1), st);
-  } else {
-    a.mtiles = (int)cdiv(M, 128);
-    launch_tm<8>(a, q4, dim3((unsigned)(a.mtiles * ntiles), 1), st);
+    hp_status s = launch_expand_q4(w, ws, st);
+    if (s != HP_OK) return s;
+    return launch_gemm16(x, ldx, ws, w.k, w.n, M, res, ldr, relu, y, ldy, st);
   }
-  return launch_ok("k_gemm");
+  return launch_gemm16(x, ldx, w.data, w.k, w.n, M, res, ldr, relu, y, ldy, st);
 }
 
 }  // namespace hp

@@ -1,0 +1,274 @@
+// fp16 x fp16 -> fp32 MFMA matrix product for tall products (the prefill
+// projections and MLP of the FlexGen layer, [FlexGen] paper notes,
+// background section; int4 weights are first expanded to FP16 once per
+// layer, as [FlexGen] section 5 prescribes, by k_expand_q4 below).
+//
+//   y[m][n] = fp16(act(sum_k x[m][k] * wt[n][k]) + res[m][n])
+//
+// Design (gfx950, wave64, v_mfma_f32_16x16x32_f16):
+//  * 512-thread workgroup = 8 waves = 2 waves per SIMD (one wave alone cannot
+//    issue MFMAs back to back), one workgroup per CU; tile 256 x 256, waves
+//    2 (rows) x 4 (columns), each wave 128 x 64 (32 accumulator tiles).
+//  * Both operands go global -> LDS with direct loads (global_load_lds,
+//    16 bytes per lane, lane l to slot l of a 1 KB chunk) into a 4-stage ring
+//    of 32-deep k-steps (32 KB per stage), three steps ahead of the MFMAs.
+//    Rows are 64 bytes; the 16-byte chunk c of row r sits in slot
+//    c ^ ((r >> 1) & 3), so fragment reads of 16 consecutive rows hit
+//    distinct banks.  The direct loads are issued from inline assembly and
+//    their completion is awaited explicitly (vmcnt) before each barrier.
+//  * Fragments of the next k-step are read from LDS while the MFMAs of the
+//    current one run.
+#include <type_traits>
+
+#include "common.h"
+#include "dequant_dev.h"
+
+namespace hp {
+
+namespace {
+
+constexpr int G_BM = 256, G_BN = 256, G_BK = 32, G_NS = 4;
+constexpr int G_STAGE = (G_BM + G_BN) * G_BK;  // halves per stage
+
+template <int N, class F>
+__device__ __forceinline__ void unroll16(F&& f) {
+  if constexpr (N > 0) {
+    unroll16<N - 1>(f);
+    f(std::integral_constant<int, N - 1>());
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One 16-byte direct load per lane into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(lds_base)
+      : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(l) (gfx9 encoding; expcnt unconstrained).
+template <int n, int l = 15>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64 && l >= 0 && l < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (l << 8) | ((n >> 4) << 14));
+}
+
+struct G16Args {
+  const _Float16* A;
+  int64_t lda, M;
+  const _Float16* W;  // wt[N][K]
+  int K, N, mtiles, ntiles;
+  const _Float16* res;
+  int64_t ldr;
+  int relu;
+  _Float16* Y;
+  int64_t ldy;
+};
+
+__global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
+  __shared__ __attribute__((aligned(1024))) _Float16 S[G_NS * G_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lives in an SGPR
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r16 = lane & 15, kq = lane >> 4;
+
+  // tile order: each XCD takes a contiguous run of tiles; runs sweep 8 row
+  // tiles per column tile so concurrent tiles share operand slices in L2
+  const int total = g.mtiles * g.ntiles;
+  int id = blockIdx.x;
+  const int per_xcd = total / 8;
+  if (id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
+  constexpr int GM = 8;
+  const int group = id / (GM * g.ntiles);
+  const int first_m = group * GM;
+  const int gm = min(GM, g.mtiles - first_m);
+  const int mt = first_m + (id % (GM * g.ntiles)) % gm;
+  const int nt = (id % (GM * g.ntiles)) / gm;
+  const int64_t m0 = (int64_t)mt * G_BM;
+  const int n0 = nt * G_BN;
+
+  // direct-load sources: this wave fills A chunks 2w, 2w+1 and B chunks
+  // 2w, 2w+1 (16 rows each); lane -> row l/4, slot l%4 holds chunk
+  // (l%4) ^ ((row >> 1) & 3)
+  const int rin = lane >> 2;
+  const int cchunk = (lane & 3) ^ ((rin >> 1) & 3);
+  const _Float16* srcA[2];
+  const _Float16* srcB[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t m = min(m0 + 16 * (2 * wave + h) + rin, g.M - 1);
+    srcA[h] = g.A + m * g.lda + 8 * cchunk;
+    const int64_t n = min(n0 + 16 * (2 * wave + h) + rin, g.N - 1);
+    srcB[h] = g.W + n * g.K + 8 * cchunk;
+  }
+  const uint32_t sbase = lds_off(S);
+  auto issue = [&](int ks, int stage) __attribute__((always_inline)) {
+    const int64_t ko = (int64_t)ks * G_BK;
+    const uint32_t st = sbase + (uint32_t)stage * G_STAGE * 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma16(srcA[h] + ko, __builtin_amdgcn_readfirstlane(st + (2 * wave + h) * 1024));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      dma16(srcB[h] + ko, __builtin_amdgcn_readfirstlane(st + G_BM * 64 + (2 * wave + h) * 1024));
+  };
+
+  f16x8 fa[2][8], fb[2][4];
+  auto read = [&](int buf, int stage) __attribute__((always_inline)) {
+    const _Float16* St = S + stage * G_STAGE;
+    const int slot = (kq ^ ((r16 >> 1) & 3)) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      fa[buf][i] = *(const f16x8*)(St + (128 * wm + 16 * i + r16) * 32 + slot);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      fb[buf][t] = *(const f16x8*)(St + G_BM * 32 + (64 * wn + 16 * t + r16) * 32 + slot);
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mma = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[buf][t], fa[buf][i], acc[i][t], 0, 0, 0);
+  };
+
+  const int KS = g.K / G_BK;
+  auto ck = [&](int ks) __attribute__((always_inline)) { return min(ks, KS - 1); };
+  // prologue: k-steps 0..3 in flight, fragments of step 0 in registers
+  issue(0, 0);
+  issue(ck(1), 1);
+  issue(ck(2), 2);
+  issue(ck(3), 3);
+  wait_vm<12>();
+  __builtin_amdgcn_s_barrier();
+  read(0, 0);
+
+  // step kk: fragments of kk in buffer kk&1; stage (kk+1)&3 must be complete
+  // (its loads were issued three steps earlier); stage kk&3 is refilled with
+  // step kk+4 once every wave has passed this step's barrier.
+  auto step = [&](int kk, auto cur_) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_)::value;
+    wait_vm<8, 0>();  // this wave's reads of stage kk are done, and its loads of kk+1
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(ck(kk + 4), kk & 3);
+    read(cur ^ 1, (kk + 1) & 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(cur);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kk = 0;
+  for (; kk + 2 <= KS; kk += 2) {
+    step(kk, std::integral_constant<int, 0>());
+    step(kk + 1, std::integral_constant<int, 1>());
+  }
+  if (kk < KS) step(kk, std::integral_constant<int, 0>());
+  wait_vm<0>();
+
+  // epilogue: lane holds rows m0 + 128 wm + 16 i + r16, columns
+  // n0 + 64 wn + 16 t + 4 kq .. +3
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + 128 * wm + 16 * i + r16;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = n0 + 64 * wn + 16 * t + 4 * kq;
+      if (n >= g.N) continue;
+      f32x4 v = acc[i][t];
+      if (g.relu) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
+      }
+      if (g.res) {
+        const f16x4 r = *(const f16x4*)(g.res + m * g.ldr + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += (float)r[e];
+      }
+      f16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (_Float16)v[e];
+      *(f16x4*)(g.Y + m * g.ldy + n) = o;
+    }
+  }
+}
+
+// Expands a packed int4 weight (see hp_mat) into wt[n][k] binary16:
+// fp16(c * scale + min) with one rounding.  One thread per 16-byte chunk of
+// the packed layout = 32 consecutive k of one output column.
+__global__ __launch_bounds__(256) void k_expand_q4(const u32x4* __restrict__ packed,
+                                                   const _Float16* __restrict__ scale,
+                                                   const _Float16* __restrict__ minv, int K, int N,
+                                                   _Float16* __restrict__ wt) {
+  const DqConst dq{0x000F000Fu, 0x00F000F0u, in_vgpr(0x64006400u), in_vgpr(0x54005400u)};
+  const int KB = K / 128;
+  const int64_t total = (int64_t)(N / 16) * KB * 64;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int L = (int)(idx & 63);
+    const int64_t tile = idx >> 6;
+    const int kb = (int)(tile % KB), nb = (int)(tile / KB);
+    const int n = 16 * nb + (L & 15);
+    const int k0 = 128 * kb + 32 * (L >> 4);
+    const u32x4 c = packed[idx];
+    const _Float16* sp = scale + (int64_t)(n >> 6) * K + k0;
+    const _Float16* mp = minv + (int64_t)(n >> 6) * K + k0;
+    _Float16* out = wt + (int64_t)n * K + k0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 s = *(const u32x4*)(sp + 8 * j);
+      const u32x4 m = *(const u32x4*)(mp + 8 * j);
+      *(f16x8*)(out + 8 * j) = dequant8(c[j], s, m, dq);
+    }
+  }
+}
+
+}  // namespace
+
+hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int k, int n, int64_t M,
+                        const void* res, int64_t ldr, bool relu, void* y, int64_t ldy,
+                        hipStream_t st) {
+  if (M == 0) return HP_OK;
+  G16Args a;
+  a.A = (const _Float16*)x;
+  a.lda = ldx;
+  a.M = M;
+  a.W = (const _Float16*)wt;
+  a.K = k;
+  a.N = n;
+  a.mtiles = (int)cdiv(M, G_BM);
+  a.ntiles = (int)cdiv(n, G_BN);
+  a.res = (const _Float16*)res;
+  a.ldr = ldr;
+  a.relu = relu ? 1 : 0;
+  a.Y = (_Float16*)y;
+  a.ldy = ldy;
+  Prof prof("gemm_f16_tiled", st);
+  hipLaunchKernelGGL(k_gemm16, dim3((unsigned)(a.mtiles * a.ntiles)), dim3(512), 0, st, a);
+  return launch_ok("k_gemm16");
+}
+
+hp_status launch_expand_q4(const hp_mat& w, void* wt, hipStream_t st) {
+  const int64_t total = (int64_t)(w.n / 16) * (w.k / 128) * 64;
+  const int blocks = (int)std::min<int64_t>(cdiv(total, 256), 65536);
+  Prof prof("expand_q4", st);
+  hipLaunchKernelGGL(k_expand_q4, dim3(blocks), dim3(256), 0, st, (const u32x4*)w.data,
+                     (const _Float16*)w.scale, (const _Float16*)w.minv, w.k, w.n, (_Float16*)wt);
+  return launch_ok("k_expand_q4");
+}
+
+}  // namespace hp

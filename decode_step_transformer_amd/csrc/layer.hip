@@ -151,11 +151,15 @@ static Ws ws_layout(const hp_dims& d) {
   const size_t Mp = (size_t)d.b * d.s, Md = (size_t)d.b * 64;
   const size_t M = std::max(Mp, Md);
   const int64_t Msk = std::min<int64_t>((int64_t)M, 144);
+  // split-k partials of skinny products, or the fp16 expansion of an int4
+  // weight for tall ones (whichever is larger)
   size_t part = 0;
-  part = std::max(part, gemm_ws_bytes(Msk, d.h1, 3 * d.h1));
-  part = std::max(part, gemm_ws_bytes(Msk, d.h1, d.h1));
-  part = std::max(part, gemm_ws_bytes(Msk, d.h1, d.h2));
-  part = std::max(part, gemm_ws_bytes(Msk, d.h2, d.h1));
+  for (int64_t mm : {Msk, (int64_t)145}) {
+    part = std::max(part, gemm_ws_bytes(mm, d.h1, 3 * d.h1, HP_Q4));
+    part = std::max(part, gemm_ws_bytes(mm, d.h1, d.h1, HP_Q4));
+    part = std::max(part, gemm_ws_bytes(mm, d.h1, d.h2, HP_Q4));
+    part = std::max(part, gemm_ws_bytes(mm, d.h2, d.h1, HP_Q4));
+  }
   Ws w;
   size_t o = 0;
   w.qkv = o; o += al(M * 3 * d.h1 * 2);
@@ -335,9 +339,9 @@ hp_status hp_pack_weight_f16(const void* w, int32_t k, int32_t n, void* wt, void
   return launch_ok("k_transpose_f16");
 }
 
-size_t hp_gemm_workspace_bytes(int64_t M, int32_t k, int32_t n) {
+size_t hp_gemm_workspace_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {
   if (M <= 0 || k <= 0 || n <= 0 || k % 128) return 0;
-  return gemm_ws_bytes(M, k, n);
+  return gemm_ws_bytes(M, k, n, fmt);
 }
 
 hp_status hp_gemm(const void* x, int64_t ldx, const hp_mat* w, int64_t M, const void* res,
@@ -355,7 +359,7 @@ hp_status hp_gemm(const void* x, int64_t ldx, const hp_mat* w, int64_t M, const 
   if (ws) NEED_ALIGN(ws, 16);
   if (ldx < w->k || ldx % 8 || ldy < w->n || ldy % 4 || (res && (ldr < w->n || ldr % 4)))
     return fail(HP_ERR_SHAPE, "row strides too small or misaligned");
-  const size_t need = gemm_ws_bytes(M, w->k, w->n);
+  const size_t need = gemm_ws_bytes(M, w->k, w->n, w->fmt);
   if (ws_bytes < need || (need && !ws))
     return fail(HP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if ((s = device_check()) != HP_OK) return s;

@@ -86,7 +86,7 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = _i32
-        L.hp_gemm_workspace_bytes.argtypes = [_i64, _i32, _i32]
+        L.hp_gemm_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32]
         L.hp_gemm_workspace_bytes.restype = _sz
         L.hp_workspace_bytes.argtypes = [C.POINTER(hp_dims)]
         L.hp_workspace_bytes.restype = _sz
@@ -195,14 +195,14 @@ def make_weight(w: torch.Tensor, fmt: int, stream=None) -> Mat:
 
 
 # ---------------------------------------------------------- layer stages
-def hp_gemm_workspace_bytes(M: int, k: int, n: int) -> int:
-    return int(lib().hp_gemm_workspace_bytes(M, k, n))
+def hp_gemm_workspace_bytes(M: int, k: int, n: int, fmt: int) -> int:
+    return int(lib().hp_gemm_workspace_bytes(M, k, n, fmt))
 
 
 def hp_gemm(x: torch.Tensor, w: Mat, res=None, relu=False, out=None, ws=None, stream=None):
     M = x.shape[0]
     y = out if out is not None else torch.empty((M, w.n), dtype=torch.float16, device=x.device)
-    need = hp_gemm_workspace_bytes(M, w.k, w.n)
+    need = hp_gemm_workspace_bytes(M, w.k, w.n, w.fmt)
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     mc = w.c()

@@ -155,8 +155,10 @@ hp_status hp_pack_weight_f16(const void* w, int32_t k, int32_t n, void* wt, void
  * act = ReLU if relu != 0.  y row stride ldy.  Sums in binary32 over k in an
  * order fixed by (k, n).  [FlexGen] background section: every projection
  * and MLP product of the layer is such a product.  ws: device scratch of at
- * least hp_gemm_workspace_bytes(M, k, n) bytes (may be NULL when that is 0). */
-size_t hp_gemm_workspace_bytes(int64_t M, int32_t k, int32_t n);
+ * least hp_gemm_workspace_bytes(M, k, n, w->fmt) bytes (may be NULL when that
+ * is 0): split-k partial sums when M <= 144, the FP16 expansion of an int4
+ * weight when M > 144. */
+size_t hp_gemm_workspace_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt);
 hp_status hp_gemm(const void* x, int64_t ldx, const hp_mat* w, int64_t M, const void* res,
                   int64_t ldr, int32_t relu, void* y, int64_t ldy, void* ws, size_t ws_bytes,
                   void* stream);
