@@ -4,20 +4,26 @@
 // converted back before use; [SpecPipe] 2.2.1-2.2.2: tree masks).
 //
 // Decode attention is HBM-bound (about 1 flop per byte of packed cache), so
-// it runs on the vector ALUs, one wave per (request, head, query):
-//  * score phase: lane = cache row; the lane streams its row's 64 bytes of
-//    codes with 16-byte loads and forms the dot product with packed
-//    fp16 dot2 on exact small-integer halves, factoring the group scale and
-//    min out of the sum: s = sum_g scale_g * (q . c)_g + min_g * (sum q)_g;
-//  * online softmax across 64-row chunks with wave reductions;
-//  * value phase: 16 lanes cover one row (one dword = 8 codes each), 4 rows
-//    at a time; sum_t p_t v_t = sum_t (p_t scale_t) c_t + sum_t p_t min_t,
-//    the second term accumulated per group in the score phase.
+// it runs on the vector ALUs, one wave per (request, head, query), streaming
+// the cache in chunks:
+//  * each lane reads 16 consecutive bytes of a row (4 lanes per int4 row of
+//    128 dims), so one load instruction covers whole rows; the loads are
+//    non-temporal and the next chunk's K (V) is requested as soon as the
+//    current chunk's scores (values) are formed;
+//  * codes become halves off + c with one and-or (off = 1024 or 64 by nibble
+//    position); in the score the offsets cancel against the accumulator's
+//    start value -sum(off q), and the group scale and min are factored out:
+//    s = sum_g scale_g (q . c)_g + min_g (sum q)_g;
+//  * online softmax over chunks with DPP reductions;
+//  * values: sum_t p_t v_t = sum_t (p_t scale_t) c_t + sum_t p_t min_t, the
+//    first term with dot2 over pairs of rows (codes of two rows per half2),
+//    the offsets removed once at the end with the sum of the weights.
 // Prefill attention reads the fresh fp16 K/V of the prompt (causal), one wave
 // per (request, head, 64 queries), lane = query, key tiles staged in LDS.
 #include <math.h>
 
 #include "common.h"
+#include "dequant_dev.h"
 #include "quant_dev.h"
 
 namespace hp {
@@ -96,168 +102,276 @@ struct DecArgs {
   _Float16* out;
 };
 
-template <int D, bool Q4>
-__global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
-  constexpr int G = D / 64;            // int4 groups per row
-  constexpr int SEGS = D / 8;          // lanes per row in the value phase
-  constexpr int RSUB = 64 / SEGS;      // rows per value-phase step
-  __shared__ float ps[64][G];          // p_t * scale_{t,g} (Q4) or p_t (F16, g = 0)
+// Cross-lane moves on the DPP path (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+constexpr int DPP_ROR = 0x120;        // + 1..15: rotate right within a row of 16 lanes
 
+// sum over aligned groups of N lanes (N = 1, 2, 4, 8, 16): every lane gets its group's sum
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<DPP_XOR1>(v);
+  if constexpr (N >= 4) v += dpp<DPP_XOR2>(v);
+  if constexpr (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+  if constexpr (N >= 16) v += dpp<DPP_MIRROR>(v);
+  return v;
+}
+// sum over the lanes congruent modulo N (N = 1, 2, 4, 8, 16): every lane gets the total
+template <int N>
+__device__ __forceinline__ float strided_sum(float v) {
+  if constexpr (N <= 1) v += dpp<DPP_ROR + 1>(v);
+  if constexpr (N <= 2) v += dpp<DPP_ROR + 2>(v);
+  if constexpr (N <= 4) v += dpp<DPP_ROR + 4>(v);
+  if constexpr (N <= 8) v += dpp<DPP_ROR + 8>(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+// wave-uniform maximum: DPP within each row of 16 lanes, then the four rows
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  const int b = __builtin_bit_cast(int, v);
+  return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+
+// Lane geometry of the streaming decode kernel.  Every lane reads 16
+// consecutive bytes of one cache row; LPR lanes cover a row, one load
+// instruction covers RPI consecutive rows and a chunk is U such loads for K
+// and for V (the next chunk is loaded while the current one is computed).
+template <int D, bool Q4>
+struct DecShape {
+  static constexpr int LPR = Q4 ? D / 32 : D / 8;
+  static constexpr int RPI = 64 / LPR;
+  static constexpr int U = (Q4 && D == 64) ? 2 : 4;
+  static constexpr int CR = U * RPI;             // rows per chunk
+  static constexpr int RB = Q4 ? D / 2 : 2 * D;  // bytes per cache row
+  static constexpr int NA = Q4 ? 32 : 8;         // value dims per lane
+};
+
+// one chunk's share of this lane: 16 code bytes per row and (Q4) the row's
+// scale/min pair of this lane's group, for K or for V
+template <int U, bool Q4>
+struct DecPart {
+  u32x4 c[U];
+  uint32_t sm[Q4 ? U : 1];
+};
+
+template <int D, bool Q4, bool MASKED>
+__global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
+  using S = DecShape<D, Q4>;
+  constexpr int LPR = S::LPR, RPI = S::RPI, U = S::U, CR = S::CR, RB = S::RB, NA = S::NA;
+  constexpr int G = D / 64;
   const int lane = threadIdx.x;
+  const int qd = lane % LPR, rho = lane / LPR;
   const int i = blockIdx.x % a.q;
   const int rh = blockIdx.x / a.q;
   const int h = rh % a.H, r = rh / a.H;
   const int P = a.pos + (a.dpos ? *a.dpos : 0);
-  const int R = a.masks ? P + a.q : P + i + 1;
-  const uint64_t mask = a.masks ? a.masks[(int64_t)r * a.q + i] : 0ull;
+  const int R = MASKED ? P + a.q : P + i + 1;
+  const uint64_t mask = MASKED ? a.masks[(int64_t)r * a.q + i] : 0ull;
+  // wave-uniform bases, per-lane 32-bit byte offsets
   const int64_t rowbase = ((int64_t)r * a.H + h) * a.cap;
-  const float scale = 1.0f / sqrtf((float)D);
+  const uint8_t* kb = (const uint8_t*)a.k + rowbase * RB;
+  const uint8_t* vb = (const uint8_t*)a.v + rowbase * RB;
+  const uint8_t* ksb = (const uint8_t*)(a.ksm + rowbase * G);
+  const uint8_t* vsb = (const uint8_t*)(a.vsm + rowbase * G);
+  const int g = Q4 ? (32 * qd) / 64 : 0;  // int4 group of this lane's dims
+  const uint32_t lane_off = 16 * qd, lane_soff = 4 * g;
+  // exp(x / sqrt(D)) = exp2(x * c2)
+  const float c2 = 1.44269504088896341f / sqrtf((float)D);
 
-  // query as binary16 pairs, in the pairing order of the score phase
-  f16x2 q2[D / 2];
-  float qsum[G];
+  const DqConst dq{0x000F000Fu, 0x00F000F0u, in_vgpr(0x64006400u), in_vgpr(0x54005400u)};
+
+  // This lane's slice of the query, paired in the order the codes expand
+  // (Q4: pair p of dword j = dims (8j+p, 8j+p+4)).  An expanded code reads
+  // off + c with off = 1024 (pairs 0, 2) or 64 (pairs 1, 3); the score
+  // accumulator starts at -sum(off * q) so that it ends at sum(c * q).
+  constexpr int NQ = Q4 ? 16 : 4;
+  f16x2 q2[NQ];
+  float corr = 0.f, qsum = 0.f;
   {
-    const uint4* qp = (const uint4*)(a.qkv + ((int64_t)r * a.q + i) * 3 * a.h1 + h * D);
+    const _Float16* qp = a.qkv + ((int64_t)r * a.q + i) * 3 * a.h1 + h * D + (Q4 ? 32 : 8) * qd;
 #pragma unroll
-    for (int g = 0; g < G; ++g) qsum[g] = 0.f;
+    for (int j = 0; j < NQ / 4; ++j) {
+      const f16x8 qh = *(const f16x8*)(qp + 8 * j);
 #pragma unroll
-    for (int w = 0; w < D / 8; ++w) {
-      const uint4 raw = qp[w];
-      const f16x8 qh = __builtin_bit_cast(f16x8, raw);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qsum[(8 * w) / 64] += (float)qh[e];
-      if constexpr (Q4) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) q2[4 * w + p] = f16x2{qh[p], qh[p + 4]};
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) q2[4 * w + p] = f16x2{qh[2 * p], qh[2 * p + 1]};
+      for (int p = 0; p < 4; ++p) {
+        if constexpr (Q4) {
+          q2[4 * j + p] = f16x2{qh[p], qh[p + 4]};
+          const float off = (p & 1) ? 64.f : 1024.f;
+          corr += off * ((float)qh[p] + (float)qh[p + 4]);
+          qsum += (float)qh[p] + (float)qh[p + 4];
+        } else {
+          q2[4 * j + p] = f16x2{qh[2 * p], qh[2 * p + 1]};
+        }
       }
     }
+    if constexpr (Q4) qsum = group_sum<LPR / G>(qsum);  // sum of q over this lane's group
   }
 
-  const int rsub = lane / SEGS, seg = lane % SEGS;
-  const int gl = (8 * seg) / 64;       // group of this lane's value dims
-  float acc[8];
+  float acc[NA];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  float pm[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) pm[g] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const f16x2 off1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  for (int e = 0; e < NA; ++e) acc[e] = 0.f;
+  float bsum = 0.f, pm = 0.f;  // Q4: sum of the fp16 weights p*scale, sum of p*min (this group)
+  float m_run = -INFINITY, l_lane = 0.f;
 
-  for (int base = 0; base < R; base += 64) {
-    const int row = base + lane;
-    const bool valid =
-        row < R && (!a.masks || row < P || ((mask >> (unsigned)(row - P)) & 1ull));
-    float s = -INFINITY;
-    float vs[G], vm[G];
+  // rows past the visible range are clamped to its last row (their weight is 0)
+  auto load = [&](DecPart<U, Q4>& X, const uint8_t* cb, const uint8_t* sb, int c) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) vs[g] = vm[g] = 0.f;
-    if (valid) {
-      if constexpr (Q4) {
-        const uint4* kp = (const uint4*)((const uint8_t*)a.k + (rowbase + row) * (D / 2));
-        uint4 kc[D / 32];
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) kc[c] = kp[c];
-        float dot[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) dot[g] = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          const uint32_t ws[4] = {kc[c].x, kc[c].y, kc[c].z, kc[c].w};
-#pragma unroll
-          for (int wj = 0; wj < 4; ++wj) {
-            const int w = 4 * c + wj;  // dword index within the row: elements 8w .. 8w+7
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const uint32_t u = ((ws[wj] >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-              const f16x2 cc = h2_of(u) - off1024;
-              dot[(8 * w) / 64] = __builtin_amdgcn_fdot2(cc, q2[4 * w + p], dot[(8 * w) / 64], false);
-            }
-          }
-        }
-        s = 0.f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const uint32_t ksm = a.ksm[(rowbase + row) * G + g];
-          const float sc = (float)h2_of(ksm)[0], mn = (float)h2_of(ksm)[1];
-          s += sc * dot[g] + mn * qsum[g];
-          const uint32_t vsm = a.vsm[(rowbase + row) * G + g];
-          vs[g] = (float)h2_of(vsm)[0];
-          vm[g] = (float)h2_of(vsm)[1];
-        }
-      } else {
-        const uint4* kp = (const uint4*)((const _Float16*)a.k + (rowbase + row) * D);
-        float dot = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-          const uint4 kv = kp[c];
-          const uint32_t ws[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-          for (int p = 0; p < 4; ++p) dot = __builtin_amdgcn_fdot2(h2_of(ws[p]), q2[4 * c + p], dot, false);
-        }
-        s = dot;
-      }
-      s *= scale;
+    for (int u = 0; u < U; ++u) {
+      const uint32_t row = (uint32_t)min(c * CR + rho + RPI * u, R - 1);
+      // the cache is streamed once per step: non-temporal loads keep it from
+      // displacing reusable lines in the caches
+      X.c[u] = __builtin_nontemporal_load((const u32x4*)(cb + (row * RB + lane_off)));
+      if constexpr (Q4) X.sm[u] = *(const uint32_t*)(sb + (row * (4 * G) + lane_soff));
     }
-    const float cmax = wave_max(s);
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
-    const float p = valid ? expf(s - m_new) : 0.f;
-    l_run = l_run * alpha + wave_sum(p);
+    // keeps the compiler from merging this load with the one of the previous
+    // iteration into a load at the loop head (which would undo the prefetch)
+    asm volatile("" ::: "memory");
+  };
+
+  // K and V of a chunk are loaded into one register set each; the next
+  // chunk's K is requested as soon as the scores are formed and its V as soon
+  // as the values are accumulated, so each stream is in flight while the
+  // other phase computes.
+  DecPart<U, Q4> K, V;
+  const int nc = (R + CR - 1) / CR;
+  load(K, kb, ksb, 0);
+  load(V, vb, vsb, 0);
+  for (int c = 0; c < nc; ++c) {
+    // scores
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float t;
+      if constexpr (Q4) {
+        t = -corr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = K.c[u][j], w8 = w >> 8;
+          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, w, dq.magic0)), q2[4 * j + 0], t, false);
+          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w, dq.magic1)), q2[4 * j + 1], t, false);
+          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, w8, dq.magic0)), q2[4 * j + 2], t, false);
+          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w8, dq.magic1)), q2[4 * j + 3], t, false);
+        }
+        t = group_sum<LPR / G>(t);  // sum(c * q) over the group
+        const f16x2 sm = h2_of(K.sm[u]);
+        t = fmaf((float)sm[0], t, (float)sm[1] * qsum);
+        if constexpr (G == 2) t += dpp<DPP_XOR2>(t);
+      } else {
+        t = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t = __builtin_amdgcn_fdot2(h2_of(K.c[u][j]), q2[j], t, false);
+        t = group_sum<LPR>(t);
+      }
+      const int row = c * CR + rho + RPI * u;
+      bool valid = row < R;
+      if constexpr (MASKED)
+        valid = valid & ((row < P) | (bool)((mask >> ((unsigned)(row - P) & 63u)) & 1ull));
+      s[u] = valid ? t : -INFINITY;
+    }
+    load(K, kb, ksb, c + 1);
+    // online softmax (chunk max is wave-uniform)
+    float cm = s[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u]);
+    cm = wave_max_dpp(cm);
+    const float m_new = fmaxf(m_run, cm);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float mc = -m_use * c2;
+    const float alpha = __builtin_amdgcn_exp2f(fmaf(m_run, c2, mc));
     m_run = m_new;
+    float p[U], ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    for (int u = 0; u < U; ++u) {
+      p[u] = __builtin_amdgcn_exp2f(fmaf(s[u], c2, mc));
+      ps += p[u];
+    }
+    l_lane = fmaf(l_lane, alpha, ps);
+    if (alpha != 1.f) {
+#pragma unroll
+      for (int e = 0; e < NA; ++e) acc[e] *= alpha;
+      bsum *= alpha;
+      pm *= alpha;
+    }
+    // values
     if constexpr (Q4) {
+      _Float16 bw[U];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        pm[g] = pm[g] * alpha + p * vm[g];
-        ps[lane][g] = p * vs[g];
+      for (int u = 0; u < U; ++u) {
+        const f16x2 sm = h2_of(V.sm[u]);
+        bw[u] = (_Float16)(p[u] * (float)sm[0]);
+        bsum += (float)bw[u];
+        pm = fmaf(p[u], (float)sm[1], pm);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u += 2) {
+        const f16x2 bb = {bw[u], bw[u + 1]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x = V.c[u][j], y = V.c[u + 1][j];
+          // halves = (row u, row u+1): codes 8j..8j+3, then 8j+4..8j+7
+          // byte permutes: p0 = (x.b0, x.b1, y.b0, y.b1), p1 = (x.b2, x.b3, y.b2, y.b3)
+          const uint32_t p0 = __builtin_amdgcn_perm(y, x, 0x05040100u);
+          const uint32_t p1 = __builtin_amdgcn_perm(y, x, 0x07060302u);
+          const uint32_t p0s = p0 >> 8, p1s = p1 >> 8;
+          float* A = acc + 8 * j;
+          A[0] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, p0, dq.magic0)), bb, A[0], false);
+          A[1] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, p0, dq.magic1)), bb, A[1], false);
+          A[2] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, p0s, dq.magic0)), bb, A[2], false);
+          A[3] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, p0s, dq.magic1)), bb, A[3], false);
+          A[4] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, p1, dq.magic0)), bb, A[4], false);
+          A[5] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, p1, dq.magic1)), bb, A[5], false);
+          A[6] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, p1s, dq.magic0)), bb, A[6], false);
+          A[7] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, p1s, dq.magic1)), bb, A[7], false);
+        }
       }
     } else {
-      ps[lane][0] = p;
-    }
-    __syncthreads();
-    const int rows = min(64, R - base);
-    for (int t = rsub; t < rows; t += RSUB) {
-      const int64_t vrow = rowbase + base + t;
-      if constexpr (Q4) {
-        const uint32_t w = *(const uint32_t*)((const uint8_t*)a.v + vrow * (D / 2) + 4 * seg);
-        const float pw = ps[t][gl];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += pw * (float)((w >> (4 * e)) & 15u);
-      } else {
-        const uint4 vv = *(const uint4*)((const _Float16*)a.v + vrow * D + 8 * seg);
-        const f16x8 vh = __builtin_bit_cast(f16x8, vv);
-        const float pw = ps[t][0];
+      for (int u = 0; u < U; ++u) {
+        const f16x8 vh = __builtin_bit_cast(f16x8, V.c[u]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += pw * (float)vh[e];
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf((float)vh[e], p[u], acc[e]);
       }
     }
-    __syncthreads();
+    load(V, vb, vsb, c + 1);
   }
 
-  // combine the RSUB row groups, then the per-group min term
+  // combine the row slots; every row's weight was counted by its LPR lanes
+  const float l = strided_sum<1>(l_lane) * (1.0f / LPR);
 #pragma unroll
-  for (int off = SEGS; off < 64; off <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
-  float pmg = 0.f;
+  for (int e = 0; e < NA; ++e) acc[e] = strided_sum<LPR>(acc[e]);
   if constexpr (Q4) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float t = wave_sum(pm[g]);
-      if (g == gl) pmg = t;
-    }
+    bsum = strided_sum<LPR>(bsum);
+    pm = strided_sum<LPR>(pm);
   }
-  if (rsub == 0) {
-    const float inv = 1.0f / l_run;
-    f16x8 o;
+  if (rho == 0) {
+    const float inv = 1.0f / l;
+    _Float16* o = a.out + ((int64_t)r * a.q + i) * a.h1 + h * D + (Q4 ? 32 : 8) * qd;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (_Float16)((acc[e] + pmg) * inv);
-    *(f16x8*)(a.out + ((int64_t)r * a.q + i) * a.h1 + h * D + 8 * seg) = o;
+    for (int j = 0; j < NA / 8; ++j) {
+      f16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[8 * j + e];
+        if constexpr (Q4) v = v - ((e & 1) ? 64.f : 1024.f) * bsum + pm;
+        y[e] = (_Float16)(v * inv);
+      }
+      *(f16x8*)(o + 8 * j) = y;
+    }
   }
 }
 
@@ -430,16 +544,14 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
   const int D = h1 / heads;
   const dim3 grid((unsigned)((int64_t)b * heads * q));
   Prof prof(kv.fmt == HP_Q4 ? "attn_decode_q4" : "attn_decode_f16", st);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, a); };
+  const bool m = masks != nullptr, q4 = kv.fmt == HP_Q4;
   if (D == 128) {
-    if (kv.fmt == HP_Q4)
-      hipLaunchKernelGGL((k_decode_attn<128, true>), grid, dim3(64), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_decode_attn<128, false>), grid, dim3(64), 0, st, a);
+    if (q4) m ? go(k_decode_attn<128, true, true>) : go(k_decode_attn<128, true, false>);
+    else m ? go(k_decode_attn<128, false, true>) : go(k_decode_attn<128, false, false>);
   } else {
-    if (kv.fmt == HP_Q4)
-      hipLaunchKernelGGL((k_decode_attn<64, true>), grid, dim3(64), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_decode_attn<64, false>), grid, dim3(64), 0, st, a);
+    if (q4) m ? go(k_decode_attn<64, true, true>) : go(k_decode_attn<64, true, false>);
+    else m ? go(k_decode_attn<64, false, true>) : go(k_decode_attn<64, false, false>);
   }
 }
 
