@@ -19,7 +19,9 @@
 //    output columns of one row: 8-byte stores.
 //  * Skinny products (M <= 144, the decode step) split k over workgroups;
 //    partial sums go to fp32 scratch and a second kernel adds them in split
-//    order, so the result depends only on (k, n), never on M.
+//    order, so the result depends only on (k, n), never on M.  int4 weights
+//    with more than 16 rows use the 8-wave kernel of gemm_dec.hip instead
+//    of the 4-wave kernel here.
 #include <type_traits>
 
 #include "common.h"
@@ -48,7 +50,7 @@ struct GemmArgs {
   const void* B;
   const _Float16* scale;
   const _Float16* minv;
-  int K, N, kb_per_split, mtiles;
+  int K, N, splits, mtiles;  // split s covers k-blocks [s KB / splits, (s+1) KB / splits)
   const _Float16* res;
   int64_t ldr;
   DqConst dq;
@@ -58,22 +60,13 @@ struct GemmArgs {
   float* P;  // split partials [split][M][N] or null
 };
 
-template <int TM, bool Q4>
-__global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
-  constexpr int BM = 16 * TM;
-  constexpr int NS = 3;  // LDS stages (activations, scales) and weight register slots
-  __shared__ __attribute__((aligned(16))) _Float16 As[NS][BM * LDS_ROW];
-  // per-wave int4 group scales/mins of one k-block (128 k): 64 dwords of
-  // scale pairs, then 64 dwords of min pairs
-  __shared__ __attribute__((aligned(16))) uint32_t Ssm[Q4 ? 4 : 1][NS][128];
+constexpr int NS = 3;  // LDS stages (activations, scales) and weight register slots
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int KB = g.K / BK;
+// Workgroup tile order: workgroups on the same XCD (id % 8) take a contiguous
+// run of tiles, and runs sweep 4 row tiles at a time so that concurrently
+// running tiles share activation and weight k-slices in L2.
+__device__ __forceinline__ void tile_of(const GemmArgs& g, int& mt, int& nt) {
   const int ntiles = (g.N + 255) / 256;
-
-  // tile order: workgroups on the same XCD (id % 8) take a contiguous run of
-  // tiles, and runs sweep 4 row tiles at a time so that concurrently running
-  // tiles share activation and weight k-slices in L2.
   const int total = g.mtiles * ntiles;
   int id = blockIdx.x;
   const int per_xcd = total / 8;
@@ -82,37 +75,52 @@ __global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
   const int group = id / (GM * ntiles);
   const int first_m = group * GM;
   const int gm = min(GM, g.mtiles - first_m);
-  const int mt = first_m + (id % (GM * ntiles)) % gm;
-  const int nt = (id % (GM * ntiles)) / gm;
+  mt = first_m + (id % (GM * ntiles)) % gm;
+  nt = (id % (GM * ntiles)) / gm;
+}
 
-  const int64_t m0 = (int64_t)mt * BM;
-  const int n_wave = nt * 256 + wave * 64;
+// One wave's part of a workgroup tile: TM 16-row tiles starting at row tile
+// rt0 of the workgroup's rows (from m0), times the 64 output columns of wave
+// column wcol.  All NT threads of the workgroup stage SR activation rows per
+// k-block into As (NS stages of SR x LDS_ROW halves); Ssm holds this wave's
+// int4 group scales/mins (NS stages of 64 dwords of scale pairs, then 64 of
+// min pairs).
+template <int TM, bool Q4, int NT, int SR>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, uint32_t* Ssm_,
+                                          int tid, int wcol, int rt0, int64_t m0, int nt) {
+  const int lane = tid & 63;
+  const int KB = g.K / BK;
+  auto As = [&](int stage) __attribute__((always_inline)) { return As_ + stage * (SR * LDS_ROW); };
+  auto Ssm = [&](int stage) __attribute__((always_inline)) { return Ssm_ + stage * 128; };
+  const int n_wave = nt * 256 + wcol * 64;
   const bool wave_on = n_wave < g.N;
   // a wave past the last column reloads the last group (never stored), so
   // every load is unconditional and wait counts stay static
   const int n_ld = min(n_wave, g.N - 64);
   const int split = blockIdx.y;
-  const int kb0 = split * g.kb_per_split, kb1 = kb0 + g.kb_per_split;
+  const int kb0 = split * KB / g.splits, kb1 = (split + 1) * KB / g.splits;
   auto clampk = [&](int kb) __attribute__((always_inline)) { return min(kb, kb1 - 1); };
 
-  // ---- activation tile loader: TM 16-byte chunks per thread.  Rows past M
+  // ---- activation tile loader: CH 16-byte chunks per thread.  Rows past M
   // reload row M-1 (their outputs are never stored).
-  u32x4 areg[TM];
-  // chunk c of this thread: row (tid >> 4) + 16 c, column (tid & 15) * 8
+  constexpr int CH = SR * 16 / NT;
+  static_assert(CH * NT == SR * 16, "staged rows must split evenly over the threads");
+  u32x4 areg[CH];
+  // chunk c of this thread: row (tid >> 4) + (NT / 16) c, column (tid & 15) * 8
   const _Float16* abase = g.A + (int64_t)((tid & 15) * 8);
   const int64_t arow0 = m0 + (tid >> 4);
   auto load_a = [&](int kb) __attribute__((always_inline)) {
-    unroll<TM>([&](auto c_) {
+    unroll<CH>([&](auto c_) {
       constexpr int c = decltype(c_)::value;
-      const int64_t m = min(arow0 + 16 * c, g.M - 1);
+      const int64_t m = min(arow0 + (NT / 16) * c, g.M - 1);
       areg[c] = *(const u32x4*)(abase + m * g.lda + (int64_t)kb * BK);
     });
   };
   auto store_a = [&](int stage) __attribute__((always_inline)) {
-    unroll<TM>([&](auto c_) {
+    unroll<CH>([&](auto c_) {
       constexpr int c = decltype(c_)::value;
-      const int chunk = tid + 256 * c;
-      *(u32x4*)(&As[stage][(chunk >> 4) * LDS_ROW + (chunk & 15) * 8]) = areg[c];
+      const int chunk = tid + NT * c;
+      *(u32x4*)(As(stage) + (chunk >> 4) * LDS_ROW + (chunk & 15) * 8) = areg[c];
     });
   };
 
@@ -148,7 +156,7 @@ __global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
     if constexpr (Q4) sreg = *(const u32x2*)(smsrc + (int64_t)kb * BK);
   };
   auto store_sm = [&](int stage) __attribute__((always_inline)) {
-    if constexpr (Q4) *(u32x2*)&Ssm[wave][stage][2 * lane] = sreg;
+    if constexpr (Q4) *(u32x2*)(Ssm(stage) + 2 * lane) = sreg;
   };
 
   const DqConst dq{g.dq.mask0, g.dq.mask1, in_vgpr(g.dq.magic0), in_vgpr(g.dq.magic1)};
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
   // ---- one MFMA k-step (32 deep): fragments of (stage, j) ----
   f16x8 xa[TM], xb[TM], wa[4], wb[4];
   auto read_x = [&](f16x8 (&x)[TM], int stage, int j) __attribute__((always_inline)) {
-    const _Float16* Ab = &As[stage][0] + r16 * LDS_ROW + 32 * kq + 8 * j;
+    const _Float16* Ab = As(stage) + (16 * rt0 + r16) * LDS_ROW + 32 * kq + 8 * j;
     unroll<TM>([&](auto i_) {
       constexpr int i = decltype(i_)::value;
       x[i] = *(const f16x8*)(Ab + 16 * i * LDS_ROW);
@@ -169,7 +177,7 @@ __global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
   auto make_w = [&](f16x8 (&w)[4], const Raw& R, int stage, auto j_) __attribute__((always_inline)) {
     constexpr int j = decltype(j_)::value;
     if constexpr (Q4) {
-      const uint32_t* Sb = &Ssm[wave][stage][16 * kq + 4 * j];
+      const uint32_t* Sb = Ssm(stage) + 16 * kq + 4 * j;
       const u32x4 sv = *(const u32x4*)Sb;
       const u32x4 mv = *(const u32x4*)(Sb + 64);
       unroll<4>([&](auto t_) {
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
   // ---- epilogue: lane holds rows m = m0 + 16 i + r16, columns n .. n+3 ----
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + 16 * i + r16;
+    const int64_t m = m0 + 16 * (rt0 + i) + r16;
     if (m >= g.M) continue;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -293,6 +301,19 @@ __global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
       *(f16x4*)(g.Y + m * g.ldy + n) = o;
     }
   }
+}
+
+// Products with one row tile per workgroup (or any M): 4 waves, each with all
+// TM row tiles of its 64 columns.
+template <int TM, bool Q4>
+__global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[NS * 16 * TM * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint32_t Ssm[4][NS * 128];
+  int mt, nt;
+  tile_of(g, mt, nt);
+  const int wave = threadIdx.x >> 6;
+  gemm_tile<TM, Q4, 256, 16 * TM>(g, As, Ssm[wave], threadIdx.x, wave, 0, (int64_t)mt * 16 * TM,
+                                  nt);
 }
 
 // Sums split-k partials in split order, then applies the epilogue.
@@ -324,7 +345,28 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   }
 }
 
-// Split factor for skinny products: a function of (k, n) only.
+// Split factors for skinny products: functions of (k, n) only, so a row's
+// result never depends on how many rows the product has.
+//
+// 8-wave int4 kernel (one workgroup per CU): minimise, in units of one
+// k-block's time, rounds * k-blocks per split + the split partials' traffic
+// (about 2.4e-4 k-block times per output column and split).
+static int split_rs(int32_t k, int32_t n) {
+  const int KB = k / BK;
+  const int64_t ntiles = cdiv(n, 256);
+  const double pc = 2.43e-4 * n;
+  int best = 1;
+  double best_cost = 1e300;
+  for (int s = 1; s <= KB && s <= 16; ++s) {
+    const double cost = (double)cdiv(ntiles * s, 256) * (double)cdiv(KB, s) + (s > 1 ? s * pc : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+// 4-wave kernel: at least 512 workgroups where the k-blocks allow.
 static int split_for(int32_t k, int32_t n) {
   const int KB = k / BK;
   const int ntiles = (int)cdiv(n, 256);
@@ -340,7 +382,7 @@ static int split_for(int32_t k, int32_t n) {
 size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {
   if (M <= 0) return 0;
   if (M > SKINNY_M) return fmt == HP_Q4 ? (size_t)k * (size_t)n * 2 : 0;  // fp16 expansion
-  const int s = split_for(k, n);
+  const int s = (fmt == HP_Q4 && M > 16) ? split_rs(k, n) : split_for(k, n);
   return s > 1 ? (size_t)s * (size_t)M * (size_t)n * sizeof(float) : 0;
 }
 
@@ -379,21 +421,27 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
   const int ntiles = (int)cdiv(w.n, 256);
   if (M <= SKINNY_M) {
     const int TM = (int)cdiv(M, 16);
-    const int splits = split_for(w.k, w.n);
-    a.kb_per_split = KB / splits;
+    const bool rs = q4 && TM >= 2;
+    const int splits = rs ? split_rs(w.k, w.n) : split_for(w.k, w.n);
+    a.splits = splits;
     a.mtiles = 1;
     if (splits > 1) a.P = (float*)ws;
     const dim3 grid(ntiles, splits);
-    switch (TM) {
-      case 1: launch_tm<1>(a, q4, grid, st); break;
-      case 2: launch_tm<2>(a, q4, grid, st); break;
-      case 3: launch_tm<3>(a, q4, grid, st); break;
-      case 4: launch_tm<4>(a, q4, grid, st); break;
-      case 5: launch_tm<5>(a, q4, grid, st); break;
-      case 6: launch_tm<6>(a, q4, grid, st); break;
-      case 7: launch_tm<7>(a, q4, grid, st); break;
-      case 8: launch_tm<8>(a, q4, grid, st); break;
-      default: launch_tm<9>(a, q4, grid, st); break;
+    if (rs) {
+      hp_status s = launch_gemm_dq(x, ldx, w, M, res, ldr, relu, y, ldy, splits, (float*)ws, st);
+      if (s != HP_OK) return s;
+    } else {
+      switch (TM) {
+        case 1: launch_tm<1>(a, q4, grid, st); break;
+        case 2: launch_tm<2>(a, q4, grid, st); break;
+        case 3: launch_tm<3>(a, q4, grid, st); break;
+        case 4: launch_tm<4>(a, q4, grid, st); break;
+        case 5: launch_tm<5>(a, q4, grid, st); break;
+        case 6: launch_tm<6>(a, q4, grid, st); break;
+        case 7: launch_tm<7>(a, q4, grid, st); break;
+        case 8: launch_tm<8>(a, q4, grid, st); break;
+        default: launch_tm<9>(a, q4, grid, st); break;
+      }
     }
     hp_status s = launch_ok("k_gemm");
     if (s != HP_OK || splits == 1) return s;

@@ -22,6 +22,7 @@
 
 #include "common.h"
 #include "dequant_dev.h"
+#include "lds_dma.h"
 
 namespace hp {
 
@@ -36,28 +37,6 @@ __device__ __forceinline__ void unroll16(F&& f) {
     unroll16<N - 1>(f);
     f(std::integral_constant<int, N - 1>());
   }
-}
-
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// One 16-byte direct load per lane into LDS at m0 + 16 * lane.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(g), "s"(lds_base)
-      : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(n) lgkmcnt(l) (gfx9 encoding; expcnt unconstrained).
-template <int n, int l = 15>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64 && l >= 0 && l < 16, "counter range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (l << 8) | ((n >> 4) << 14));
 }
 
 struct G16Args {
