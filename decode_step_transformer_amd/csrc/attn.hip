@@ -10,14 +10,15 @@
 //    128 dims), so one load instruction covers whole rows; the loads are
 //    non-temporal and the next chunk's K (V) is requested as soon as the
 //    current chunk's scores (values) are formed;
-//  * codes become halves off + c with one and-or (off = 1024 or 64 by nibble
-//    position); in the score the offsets cancel against the accumulator's
-//    start value -sum(off q), and the group scale and min are factored out:
-//    s = sum_g scale_g (q . c)_g + min_g (sum q)_g;
+//  * codes become halves off + c with a shift and one and-or; in the score
+//    every code reads 64 + c and the offsets cancel against the
+//    accumulator's start value -64 sum(q); the group scale and min are
+//    factored out: s = sum_g scale_g (q . c)_g + min_g (sum q)_g;
 //  * online softmax over chunks with DPP reductions;
 //  * values: sum_t p_t v_t = sum_t (p_t scale_t) c_t + sum_t p_t min_t, the
-//    first term with dot2 over pairs of rows (codes of two rows per half2),
-//    the offsets removed once at the end with the sum of the weights.
+//    first term with one mixed-precision FMA per code (binary16 off + c,
+//    fp32 weight and sum), the offsets removed once at the end with the sum
+//    of the weights.
 // Prefill attention reads the fresh fp16 K/V of the prompt (causal), one wave
 // per (request, head, 64 queries), lane = query, key tiles staged in LDS.
 #include <math.h>
@@ -196,9 +197,11 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   const DqConst dq{0x000F000Fu, 0x00F000F0u, in_vgpr(0x64006400u), in_vgpr(0x54005400u)};
 
   // This lane's slice of the query, paired in the order the codes expand
-  // (Q4: pair p of dword j = dims (8j+p, 8j+p+4)).  An expanded code reads
-  // off + c with off = 1024 (pairs 0, 2) or 64 (pairs 1, 3); the score
-  // accumulator starts at -sum(off * q) so that it ends at sum(c * q).
+  // (Q4: pair p of dword j = dims (8j+p, 8j+p+4)).  In the score an expanded
+  // code reads 64 + c (every nibble is moved to bits 4..7 of a half under the
+  // exponent of 64); the accumulator starts at -64 sum(q), so it ends at
+  // sum(c * q).  The small offset keeps the cancelled magnitude, and so the
+  // fp32 rounding of the running sum, near that of sum(c * q) itself.
   constexpr int NQ = Q4 ? 16 : 4;
   f16x2 q2[NQ];
   float corr = 0.f, qsum = 0.f;
@@ -211,8 +214,7 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
       for (int p = 0; p < 4; ++p) {
         if constexpr (Q4) {
           q2[4 * j + p] = f16x2{qh[p], qh[p + 4]};
-          const float off = (p & 1) ? 64.f : 1024.f;
-          corr += off * ((float)qh[p] + (float)qh[p + 4]);
+          corr += 64.f * ((float)qh[p] + (float)qh[p + 4]);
           qsum += (float)qh[p] + (float)qh[p + 4];
         } else {
           q2[4 * j + p] = f16x2{qh[2 * p], qh[2 * p + 1]};
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   float acc[NA];
 #pragma unroll
   for (int e = 0; e < NA; ++e) acc[e] = 0.f;
-  float bsum = 0.f, pm = 0.f;  // Q4: sum of the fp16 weights p*scale, sum of p*min (this group)
+  float bsum = 0.f, pm = 0.f;  // Q4: sum of the weights p*scale, sum of p*min (this group)
   float m_run = -INFINITY, l_lane = 0.f;
 
   // rows past the visible range are clamped to its last row (their weight is 0)
@@ -261,11 +263,12 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
         t = -corr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t w = K.c[u][j], w8 = w >> 8;
-          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, w, dq.magic0)), q2[4 * j + 0], t, false);
+          // every pair at bits 4..7 / 20..23 under the exponent of 64
+          const uint32_t w = K.c[u][j];
+          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w << 4, dq.magic1)), q2[4 * j + 0], t, false);
           t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w, dq.magic1)), q2[4 * j + 1], t, false);
-          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, w8, dq.magic0)), q2[4 * j + 2], t, false);
-          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w8, dq.magic1)), q2[4 * j + 3], t, false);
+          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w >> 4, dq.magic1)), q2[4 * j + 2], t, false);
+          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w >> 8, dq.magic1)), q2[4 * j + 3], t, false);
         }
         t = group_sum<LPR / G>(t);  // sum(c * q) over the group
         const f16x2 sm = h2_of(K.sm[u]);
@@ -309,34 +312,34 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
     }
     // values
     if constexpr (Q4) {
-      _Float16 bw[U];
+      // weights p * scale stay in fp32: each code meets its row's weight in
+      // one mixed-precision FMA (binary16 code, fp32 weight and sum)
+      float bw[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const f16x2 sm = h2_of(V.sm[u]);
-        bw[u] = (_Float16)(p[u] * (float)sm[0]);
-        bsum += (float)bw[u];
+        bw[u] = p[u] * (float)sm[0];
+        bsum += bw[u];
         pm = fmaf(p[u], (float)sm[1], pm);
       }
 #pragma unroll
-      for (int u = 0; u < U; u += 2) {
-        const f16x2 bb = {bw[u], bw[u + 1]};
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t x = V.c[u][j], y = V.c[u + 1][j];
-          // halves = (row u, row u+1): codes 8j..8j+3, then 8j+4..8j+7
-          // byte permutes: p0 = (x.b0, x.b1, y.b0, y.b1), p1 = (x.b2, x.b3, y.b2, y.b3)
-          const uint32_t p0 = __builtin_amdgcn_perm(y, x, 0x05040100u);
-          const uint32_t p1 = __builtin_amdgcn_perm(y, x, 0x07060302u);
-          const uint32_t p0s = p0 >> 8, p1s = p1 >> 8;
+          const uint32_t x = V.c[u][j], x8 = x >> 8;
+          const f16x2 c04 = h2_of(bfi(dq.mask0, x, dq.magic0));   // codes 8j, 8j+4 (+1024)
+          const f16x2 c15 = h2_of(bfi(dq.mask1, x, dq.magic1));   // codes 8j+1, 8j+5 (+64)
+          const f16x2 c26 = h2_of(bfi(dq.mask0, x8, dq.magic0));  // codes 8j+2, 8j+6 (+1024)
+          const f16x2 c37 = h2_of(bfi(dq.mask1, x8, dq.magic1));  // codes 8j+3, 8j+7 (+64)
           float* A = acc + 8 * j;
-          A[0] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, p0, dq.magic0)), bb, A[0], false);
-          A[1] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, p0, dq.magic1)), bb, A[1], false);
-          A[2] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, p0s, dq.magic0)), bb, A[2], false);
-          A[3] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, p0s, dq.magic1)), bb, A[3], false);
-          A[4] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, p1, dq.magic0)), bb, A[4], false);
-          A[5] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, p1, dq.magic1)), bb, A[5], false);
-          A[6] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask0, p1s, dq.magic0)), bb, A[6], false);
-          A[7] = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, p1s, dq.magic1)), bb, A[7], false);
+          A[0] = fmaf((float)c04[0], bw[u], A[0]);
+          A[4] = fmaf((float)c04[1], bw[u], A[4]);
+          A[1] = fmaf((float)c15[0], bw[u], A[1]);
+          A[5] = fmaf((float)c15[1], bw[u], A[5]);
+          A[2] = fmaf((float)c26[0], bw[u], A[2]);
+          A[6] = fmaf((float)c26[1], bw[u], A[6]);
+          A[3] = fmaf((float)c37[0], bw[u], A[3]);
+          A[7] = fmaf((float)c37[1], bw[u], A[7]);
         }
       }
     } else {
