@@ -56,6 +56,7 @@ def lib():
         L.or_attention.argtypes = [_int, _int, _p, _p, _p, _p, _p, _int, _p]
         L.or_layer_prefill.argtypes = [_int] * 5 + [_p] * 7 + [_int, _int, _p, _p, _p, _p, _int, _p]
         L.or_layer_decode.argtypes = [_int] * 6 + [_p] * 8 + [_int, _int, _p, _p, _p, _p, _p]
+        L.or_kv_append.argtypes = [_int] * 5 + [_p, _p, _int, _int, _p, _p, _p, _p]
         L.or_tree_masks.restype = _int
         L.or_tree_masks.argtypes = [_p, _int, _p]
         L.or_run_block.argtypes = [_int] * 9 + [_p, _p, _p, _int, _int, _p, _p, _p, _p, _p, _p]
@@ -191,6 +192,14 @@ class KV:
         codes = getattr(self, which)[:, :, :T]
         sm = getattr(self, which + "sm")[:, :, :T]
         return dequantize_g64(codes, sm)
+
+
+def kv_append(kv: KV, k_rows, v_rows, pos: int) -> None:
+    """Stores k_rows, v_rows [b][nq][h1] (fp16) as cache rows [pos, pos + nq)."""
+    kb, vb = _bits(k_rows), _bits(v_rows)
+    b, nq, h1 = kb.shape
+    assert vb.shape == kb.shape and b == kv.b and pos + nq <= kv.cap
+    lib().or_kv_append(b, nq, h1, kv.heads, pos, _ptr(kb), _ptr(vb), *kv.args())
 
 
 def _w6(W):

@@ -258,6 +258,21 @@ static void kv_store(int fmt, int H, int d, int cap, int r, int pos, int nq, con
     }
 }
 
+// Concat of given K/V token rows into the cache ([FlexGen] background
+// section, decode: the new k and v rows are concatenated to the cache; section
+// 5: stored as int4 groups of 64 along the hidden dimension): k_rows and
+// v_rows are [b][nq][h1]; they become rows [pos, pos + nq) of every request.
+void or_kv_append(int b, int nq, int h1, int heads, int pos, const uint16_t* k_rows,
+                  const uint16_t* v_rows, int kv_fmt, int cap, void* k_store, void* v_store,
+                  uint16_t* k_sm, uint16_t* v_sm) {
+  const int d = h1 / heads;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < b; ++r) {
+    kv_store(kv_fmt, heads, d, cap, r, pos, nq, k_rows + (i64)r * nq * h1, h1, k_store, k_sm);
+    kv_store(kv_fmt, heads, d, cap, r, pos, nq, v_rows + (i64)r * nq * h1, h1, v_store, v_sm);
+  }
+}
+
 // Read rows [0, T) of request r, head h, as fp16 values dst[T][d].
 static void kv_load(int fmt, int H, int d, int cap, int r, int h, int T, const void* store,
                     const uint16_t* sm, uint16_t* dst) {

@@ -10,9 +10,18 @@ Generator: a counter-based SplitMix64 stream (Steele, Lea and Flood,
 with key = mix64(seed * P + stream), G the golden-ratio increment
 0x9E3779B97F4A7C15 and mix64 the SplitMix64 finaliser.  Normal deviates come
 from the Box-Muller transform (Box and Muller, 1958) applied to pairs of
-words; each is scaled by sigma and rounded to IEEE binary16 by numpy.
+words; each is scaled by sigma and rounded to IEEE binary16 by numpy.  The
+words and the normals in binary64 come from synth/gen.c (OpenMP, built on
+first use), so full-size tensors take seconds; `words` below is the same
+generator in numpy, kept as the reference that the C build is checked
+against.
 """
 from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
 
 import numpy as np
 
@@ -20,7 +29,7 @@ _G = np.uint64(0x9E3779B97F4A7C15)
 _P = np.uint64(0xD1B54A32D192ED03)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
-_CHUNK = 1 << 22
+_CHUNK = 1 << 24
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -43,20 +52,62 @@ def words(seed: int, stream: int, start: int, count: int) -> np.ndarray:
         return _mix64(key + idx * _G)
 
 
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = False) -> str:
+    """Compiles synth/gen.c into synth/libsynth.so (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + f".{os.getpid()}.tmp"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+                        "-ffp-contract=off", "-Wall", os.path.join(_HERE, "gen.c"), "-lm",
+                        "-o", tmp], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _native():
+    global _lib
+    with _lock:
+        if _lib is None:
+            L = ctypes.CDLL(build())
+            L.syn_words.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_void_p]
+            L.syn_normal.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_double, ctypes.c_void_p]
+            _lib = L
+    return _lib
+
+
+def words_native(seed: int, stream: int, start: int, count: int) -> np.ndarray:
+    """The same words as `words`, from the C build."""
+    out = np.empty(count, dtype=np.uint64)
+    _native().syn_words(seed, stream, start, count, out.ctypes.data)
+    return out
+
+
 def normal_f16(seed: int, stream: int, shape, sigma: float = 1.0) -> np.ndarray:
     """N(0, sigma^2) samples rounded to binary16, C order, element i uses words 2i, 2i+1."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float16)
+    L = _native()
+    buf = np.empty(min(n, _CHUNK), dtype=np.float64)
     for lo in range(0, n, _CHUNK):
         m = min(_CHUNK, n - lo)
-        w = words(seed, stream, 2 * lo, 2 * m)
-        a = w[0::2]
-        b = w[1::2]
-        u1 = ((a >> np.uint64(11)).astype(np.float64) + 0.5) * (2.0 ** -53)
-        u2 = (b >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
-        z = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
-        out[lo:lo + m] = (z * sigma).astype(np.float16)
+        L.syn_normal(seed, stream, lo, m, float(sigma), buf.ctypes.data)
+        out[lo:lo + m] = buf[:m].astype(np.float16)
     return out.reshape(shape)
+
+
+def normal_f64_reference(seed: int, stream: int, start: int, count: int) -> np.ndarray:
+    """Box-Muller normals (sigma 1) of elements [start, start+count) in numpy."""
+    w = words(seed, stream, 2 * start, 2 * count)
+    u1 = ((w[0::2] >> np.uint64(11)).astype(np.float64) + 0.5) * (2.0 ** -53)
+    u2 = (w[1::2] >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
 
 
 def uniform_bits(seed: int, stream: int, count: int) -> np.ndarray:
@@ -114,3 +165,12 @@ STREAM_TREE_Q, STREAM_TREE_K, STREAM_TREE_V = 3_000_000, 3_000_001, 3_000_002
 
 def stream_layer_input(layer: int) -> int:
     return 4_000_000 + layer
+
+
+# Per-request streams (full-size parity tests draw only the sampled requests).
+_REQUEST_KINDS = {"prompt": 6_000_000, "token": 7_000_000, "cache_k": 8_000_000,
+                  "cache_v": 9_000_000, "tree_qkv": 10_000_000}
+
+
+def stream_request(kind: str, request: int) -> int:
+    return _REQUEST_KINDS[kind] + int(request)

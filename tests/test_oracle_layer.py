@@ -14,6 +14,8 @@ import numpy as np
 import pytest
 import scipy.special
 
+import synth
+
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -261,3 +263,26 @@ def test_block_equals_layer_composition(orc):
         for j in range(l):
             cur = orc.layer_decode(cur, layers[j], kv2[j], H, s + i)
         assert np.array_equal(cur[:, 0].view(np.uint16), to[i].view(np.uint16))
+
+
+def test_kv_append_layout(orc):
+    """Appended rows land head-major at [pos, pos+nq), coded like the quantiser."""
+    b, nq, heads, d, pos = 2, 3, 2, 128, 5
+    h1 = heads * d
+    k = synth.normal_f16(91, 1, (b, nq, h1))
+    v = synth.normal_f16(91, 2, (b, nq, h1))
+    for fmt in (orc.F16, orc.Q4):
+        kv = orc.KV(fmt, b, heads, pos + nq + 1, d)
+        orc.kv_append(kv, k, v, pos)
+        for r in range(b):
+            for h in range(heads):
+                for i in range(nq):
+                    for name, src in (("k", k), ("v", v)):
+                        row = src[r, i, h * d:(h + 1) * d]
+                        if fmt == orc.F16:
+                            assert np.array_equal(getattr(kv, name)[r, h, pos + i].view(np.float16), row)
+                        else:
+                            c, sm = orc.quantize_g64(row[None, :])
+                            assert np.array_equal(getattr(kv, name)[r, h, pos + i], c[0])
+                            assert np.array_equal(getattr(kv, name + "sm")[r, h, pos + i], sm[0])
+        assert not getattr(kv, "k")[:, :, :pos].any() and not getattr(kv, "k")[:, :, pos + nq:].any()
