@@ -19,12 +19,13 @@
 //    first term with one mixed-precision FMA per code (binary16 off + c,
 //    fp32 weight and sum), the offsets removed once at the end with the sum
 //    of the weights.
-// Prefill attention reads the fresh fp16 K/V of the prompt (causal), one wave
-// per (request, head, 64 queries), lane = query, key tiles staged in LDS.
+// Prefill attention reads the fresh fp16 K/V of the prompt (causal) on MFMA;
+// see the section below.
 #include <math.h>
 
 #include "common.h"
 #include "dequant_dev.h"
+#include "lds_dma.h"
 #include "quant_dev.h"
 
 namespace hp {
@@ -379,108 +380,188 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
 }
 
 // ------------------------------------------------------ prefill attention
-// Causal attention over the fresh K/V of the prompt: query i sees keys 0..i.
-constexpr int PF_KT = 16;  // keys per LDS tile
+// Causal attention over the fresh fp16 K/V of the prompt (query i sees keys
+// 0..i), on MFMA (v_mfma_f32_16x16x32_f16), flash-attention style.
+//  * Workgroup = 4 waves = 64 queries of one (request, head); wave w owns
+//    queries 16 w .. 16 w + 15.  Key blocks of 64 rows of K and V go to LDS
+//    by direct loads (double-buffered) and serve all 4 waves.
+//  * Scores S^T = K Q^T: operand A = 16 keys x 32 dims of K (one 16-byte
+//    LDS read per lane; 16-byte chunks XOR-swizzled by key), operand B = the
+//    wave's Q fragments, held in registers.  Lane l then holds 16 scores of
+//    query l % 16, so the online-softmax state is per lane.
+//  * The key rows of each 16-key score tile are permuted so that lane group
+//    l / 16 ends up with 8 consecutive keys per 32-key step: exactly the
+//    operand-B layout of the value product.
+//  * Output O^T = V^T P^T: operand A = 16 dims x 32 keys of V^T, read with
+//    the transposing LDS read ds_read_b64_tr_b16 (two reads of 4 keys; V's
+//    chunks are XOR-swizzled so the 4 rows of one read hit distinct banks),
+//    operand B = the probabilities as binary16; lane l accumulates 4 dims
+//    of query l % 16 per 16-dim block.
+constexpr int PF_QB = 64;  // queries per workgroup
+constexpr int PF_KB = 64;  // keys per block
+
+struct PfArgs {
+  const _Float16* qkv;
+  int s, h1, H;
+  _Float16* out;
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 ds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const __attribute__((address_space(3))) void*)p);
+}
 
 template <int D>
-__global__ __launch_bounds__(64) void k_prefill_attn(const _Float16* __restrict__ qkv, int s,
-                                                     int h1, int H, _Float16* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) _Float16 Ks[PF_KT][D];
-  __shared__ __attribute__((aligned(16))) _Float16 Vs[PF_KT][D];
-  const int lane = threadIdx.x;
-  const int nqb = (s + 63) / 64;
-  const int qb = blockIdx.x % nqb;
-  const int rh = blockIdx.x / nqb;
-  const int h = rh % H, r = rh / H;
-  const int qi = qb * 64 + lane;
-  const bool qv = qi < s;
-  const int64_t ld = 3LL * h1;
-  const _Float16* base = qkv + (int64_t)r * s * ld + h * D;
-  const float scale = 1.0f / sqrtf((float)D);
+__global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
+  constexpr int KS = D / 32;           // k-steps of the score product
+  constexpr int DB = D / 16;           // 16-dim output blocks
+  constexpr int RB = 2 * D;            // bytes per key row in LDS
+  constexpr int SPR = RB / 16;         // 16-byte slots per row
+  constexpr int KPI = 64 / SPR;        // key rows per direct load (1 KB)
+  constexpr int NI = PF_KB / KPI / 4;  // direct loads per wave per block, for K and for V
+  constexpr int STAGE = 2 * PF_KB * RB;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
-  f16x2 q2[D / 2];
+  const int lane = threadIdx.x & 63, r16 = lane & 15, G = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s = a.s;
+  const int nqb = (s + PF_QB - 1) / PF_QB;
+  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);  // longest query blocks first
+  const int rh = blockIdx.x / nqb;
+  const int h = rh % a.H, r = rh / a.H;
+  const int64_t ld = 3LL * a.h1;
+  const _Float16* base = a.qkv + (int64_t)r * s * ld + h * D;
+  const int qi = qb * PF_QB + 16 * wave + r16;  // this lane's query
+  const float c2 = 1.44269504088896341f / sqrtf((float)D);
+
+  // Q fragments (operand B of the score product): dims 8 G + 32 ks .. +7
+  f16x8 qf[KS];
   {
-    const uint4* qp = (const uint4*)(base + (int64_t)(qv ? qi : 0) * ld);
+    const _Float16* qp = base + (int64_t)min(qi, s - 1) * ld + 8 * G;
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const uint4 raw = qp[c];
-      q2[4 * c + 0] = h2_of(raw.x);
-      q2[4 * c + 1] = h2_of(raw.y);
-      q2[4 * c + 2] = h2_of(raw.z);
-      q2[4 * c + 3] = h2_of(raw.w);
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const f16x8*)(qp + 32 * ks);
   }
-  float acc[D];
+
+  // swizzles: K slot = chunk ^ fk(key) (16 keys of a score tile distinct),
+  // V slot = chunk ^ 2 (key & 3) (4 rows of a transposing read distinct)
+  auto fk = [](int key) __attribute__((always_inline)) {
+    return ((key & 3) | (((key >> 3) & 3) << 2)) & (SPR - 1);
+  };
+  auto fv = [](int key) __attribute__((always_inline)) { return ((key & 3) << 1) & (SPR - 1); };
+
+  const uint32_t lbase = lds_off(lds);
+  const int nkb = min(qb + 1, (s + PF_KB - 1) / PF_KB);
+  auto issue = [&](int kb, int st) __attribute__((always_inline)) {
 #pragma unroll
-  for (int c = 0; c < D; ++c) acc[c] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const int kend = min(s, qb * 64 + 64);
-  for (int k0 = 0; k0 < kend; k0 += PF_KT) {
-    __syncthreads();
-    // stage PF_KT rows of K and V: PF_KT * D / 8 16-byte chunks each
-    for (int c = lane; c < PF_KT * D / 8; c += 64) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (k0 + row < s) {
-        kv = *(const uint4*)(base + (int64_t)(k0 + row) * ld + h1 + col);
-        vv = *(const uint4*)(base + (int64_t)(k0 + row) * ld + 2 * h1 + col);
+    for (int i = 0; i < NI; ++i) {
+      const int u = wave * NI + i;
+      const int key = KPI * u + lane / SPR;  // key within the block
+      const int slot = lane % SPR;
+      const int row = min(kb * PF_KB + key, s - 1);
+      const _Float16* src = base + (int64_t)row * ld;
+      dma16(src + a.h1 + 8 * (slot ^ fk(key)),
+            __builtin_amdgcn_readfirstlane(lbase + st * STAGE + u * 1024));
+      dma16(src + 2 * a.h1 + 8 * (slot ^ fv(key)),
+            __builtin_amdgcn_readfirstlane(lbase + st * STAGE + PF_KB * RB + u * 1024));
+    }
+  };
+
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+
+  issue(0, 0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int st = kb & 1;
+    wait_vm<0, 0>();
+    __builtin_amdgcn_s_barrier();
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+    const uint8_t* Kl = lds + st * STAGE;
+    const uint8_t* Vl = Kl + PF_KB * RB;
+
+    // scores of 4 tiles of 16 keys; tile T row m holds key
+    // 32 (T / 2) + 8 (m / 4) + 4 (T % 2) + m % 4
+    f32x4 sc[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int key = 32 * (T / 2) + 8 * (r16 / 4) + 4 * (T % 2) + (r16 % 4);
+      const uint8_t* kr = Kl + key * RB;
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const f16x8 kf = *(const f16x8*)(kr + 16 * ((G + 4 * ks) ^ fk(key)));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], c, 0, 0, 0);
       }
-      *(uint4*)&Ks[row][col] = kv;
-      *(uint4*)&Vs[row][col] = vv;
+      sc[T] = c;
     }
-    __syncthreads();
-    float sc[PF_KT];
-    float cmax = -INFINITY;
+    // mask (causal and past the prompt), block maximum per query
+    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < PF_KT; ++j) {
-      const int kj = k0 + j;
-      float dot = 0.f;
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const uint4 kv = *(const uint4*)&Ks[j][8 * c];
-        dot = __builtin_amdgcn_fdot2(h2_of(kv.x), q2[4 * c + 0], dot, false);
-        dot = __builtin_amdgcn_fdot2(h2_of(kv.y), q2[4 * c + 1], dot, false);
-        dot = __builtin_amdgcn_fdot2(h2_of(kv.z), q2[4 * c + 2], dot, false);
-        dot = __builtin_amdgcn_fdot2(h2_of(kv.w), q2[4 * c + 3], dot, false);
+      for (int e = 0; e < 4; ++e) {
+        const int kidx = kb * PF_KB + 32 * (T / 2) + 8 * G + 4 * (T % 2) + e;
+        if (kidx > qi || kidx >= s) sc[T][e] = -INFINITY;
+        mx = fmaxf(mx, sc[T][e]);
       }
-      sc[j] = (kj <= qi && kj < s) ? dot * scale : -INFINITY;
-      cmax = fmaxf(cmax, sc[j]);
-    }
-    const float m_new = fmaxf(m_run, cmax);
-    if (m_new == -INFINITY) continue;  // no visible key yet for this lane
-    const float alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < PF_KT; ++j) {
-      sc[j] = (sc[j] == -INFINITY) ? 0.f : expf(sc[j] - m_new);
-      psum += sc[j];
-    }
-    l_run = l_run * alpha + psum;
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float mc = -m_use * c2;
+    const float alpha = __builtin_amdgcn_exp2f(fmaf(m_run, c2, mc));
     m_run = m_new;
+    float ps = 0.f;
+    f16x8 pb[2];
 #pragma unroll
-    for (int c = 0; c < D; c += 8) {
-      float a8[8];
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a8[e] = acc[c + e] * alpha;
-#pragma unroll
-      for (int j = 0; j < PF_KT; ++j) {
-        const f16x8 vh = *(const f16x8*)&Vs[j][c];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a8[e] += sc[j] * (float)vh[e];
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[T][e], c2, mc));
+        ps += p;
+        pb[T / 2][4 * (T % 2) + e] = (_Float16)p;
       }
+    l_lane = fmaf(l_lane, alpha, ps);
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[c + e] = a8[e];
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    // O^T += V^T P^T over two 32-key steps
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f16x8 vf;
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+          const int row = 32 * p + 8 * G + 4 * n2 + r16 / 4;
+          const int d = 16 * db + 4 * (r16 % 4);
+          const uint8_t* vp = Vl + row * RB + 16 * ((d / 8) ^ fv(row)) + 2 * (d % 8);
+          const s16x4 t = ds_read_tr16(vp);
+          const f16x4 th = __builtin_bit_cast(f16x4, t);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vf[4 * n2 + e] = th[e];
+        }
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[p], o[db], 0, 0, 0);
+      }
     }
   }
-  if (!qv) return;
-  const float inv = 1.0f / l_run;
-  _Float16* o = out + ((int64_t)r * s + qi) * h1 + h * D;
+  wait_vm<0>();
+  // the 4 lanes of a query hold complementary key subsets: total their sums
+  float l = l_lane + __shfl_xor(l_lane, 16);
+  l += __shfl_xor(l, 32);
+  if (qi >= s) return;
+  const float inv = 1.0f / l;
+  _Float16* op = a.out + ((int64_t)r * s + qi) * a.h1 + h * D + 4 * G;
 #pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    f16x8 v8;
+  for (int db = 0; db < DB; ++db) {
+    f16x4 y;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v8[e] = (_Float16)(acc[c + e] * inv);
-    *(f16x8*)(o + c) = v8;
+    for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[db][e] * inv);
+    *(f16x4*)(op + 16 * db) = y;
   }
 }
 
@@ -561,14 +642,13 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
 void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, const void* qkv,
                               void* out, hipStream_t st) {
   const int D = h1 / heads;
-  const dim3 grid((unsigned)((int64_t)b * heads * cdiv(s, 64)));
+  const dim3 grid((unsigned)((int64_t)b * heads * cdiv(s, PF_QB)));
+  PfArgs a{(const _Float16*)qkv, s, h1, heads, (_Float16*)out};
   Prof prof("attn_prefill", st);
   if (D == 128)
-    hipLaunchKernelGGL(k_prefill_attn<128>, grid, dim3(64), 0, st, (const _Float16*)qkv, s, h1,
-                       heads, (_Float16*)out);
+    hipLaunchKernelGGL(k_prefill_attn<128>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_prefill_attn<64>, grid, dim3(64), 0, st, (const _Float16*)qkv, s, h1,
-                       heads, (_Float16*)out);
+    hipLaunchKernelGGL(k_prefill_attn<64>, grid, dim3(256), 0, st, a);
 }
 
 void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
