@@ -413,6 +413,111 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const void* p) {
       (__attribute__((address_space(3))) s16x4*)(const __attribute__((address_space(3))) void*)p);
 }
 
+// Chunk swizzles of the fp16 K and V tiles (SPR 16-byte slots per row): the
+// 16 keys of a score tile, and the 4 rows of one transposing read, fall in
+// distinct banks.
+template <int SPR>
+__device__ __forceinline__ int swz_k(int key) {
+  return ((key & 3) | (((key >> 3) & 3) << 2)) & (SPR - 1);
+}
+template <int SPR>
+__device__ __forceinline__ int swz_v(int key) {
+  return ((key & 3) << 1) & (SPR - 1);
+}
+
+// One block of 64 keys for the 16 queries of a wave (query l % 16 per lane):
+// scores S^T = K Q^T, keys with !visible(kidx) masked, online softmax, and
+// O^T += V^T P^T.  Kl, Vl: fp16 tiles of the block (64 rows of 2 D bytes).
+template <int D, class Vis>
+__device__ __forceinline__ void flash_block(const uint8_t* Kl, const uint8_t* Vl,
+                                            const f16x8 (&qf)[D / 32], int k0, Vis visible,
+                                            float c2, float& m_run, float& l_lane,
+                                            f32x4 (&o)[D / 16]) {
+  constexpr int KS = D / 32, DB = D / 16, RB = 2 * D, SPR = RB / 16;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, G = lane >> 4;
+  // scores of 4 tiles of 16 keys; tile T row m holds key
+  // 32 (T / 2) + 8 (m / 4) + 4 (T % 2) + m % 4
+  f32x4 sc[4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const int key = 32 * (T / 2) + 8 * (r16 / 4) + 4 * (T % 2) + (r16 % 4);
+    const uint8_t* kr = Kl + key * RB;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f16x8 kf = *(const f16x8*)(kr + 16 * ((G + 4 * ks) ^ swz_k<SPR>(key)));
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], c, 0, 0, 0);
+    }
+    sc[T] = c;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!visible(k0 + 32 * (T / 2) + 8 * G + 4 * (T % 2) + e)) sc[T][e] = -INFINITY;
+      mx = fmaxf(mx, sc[T][e]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float mc = -m_use * c2;
+  const float alpha = __builtin_amdgcn_exp2f(fmaf(m_run, c2, mc));
+  m_run = m_new;
+  float ps = 0.f;
+  f16x8 pb[2];
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[T][e], c2, mc));
+      ps += p;
+      pb[T / 2][4 * (T % 2) + e] = (_Float16)p;
+    }
+  l_lane = fmaf(l_lane, alpha, ps);
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  }
+  // O^T += V^T P^T over two 32-key steps
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f16x8 vf;
+#pragma unroll
+      for (int n2 = 0; n2 < 2; ++n2) {
+        const int row = 32 * p + 8 * G + 4 * n2 + r16 / 4;
+        const int d = 16 * db + 4 * (r16 % 4);
+        const uint8_t* vp = Vl + row * RB + 16 * ((d / 8) ^ swz_v<SPR>(row)) + 2 * (d % 8);
+        const f16x4 th = __builtin_bit_cast(f16x4, ds_read_tr16(vp));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vf[4 * n2 + e] = th[e];
+      }
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[p], o[db], 0, 0, 0);
+    }
+  }
+}
+
+// Normalised output of a wave's 16 queries: lane l holds dims 16 db + 4 (l / 16) + e.
+template <int D>
+__device__ __forceinline__ void flash_store(_Float16* row, float l_lane, const f32x4 (&o)[D / 16]) {
+  const int G = (threadIdx.x & 63) >> 4;
+  // the 4 lanes of a query hold complementary key subsets: total their sums
+  float l = l_lane + __shfl_xor(l_lane, 16);
+  l += __shfl_xor(l, 32);
+  if (!row) return;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    f16x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[db][e] * inv);
+    *(f16x4*)(row + 16 * db + 4 * G) = y;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
   constexpr int KS = D / 32;           // k-steps of the score product
@@ -444,13 +549,6 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const f16x8*)(qp + 32 * ks);
   }
 
-  // swizzles: K slot = chunk ^ fk(key) (16 keys of a score tile distinct),
-  // V slot = chunk ^ 2 (key & 3) (4 rows of a transposing read distinct)
-  auto fk = [](int key) __attribute__((always_inline)) {
-    return ((key & 3) | (((key >> 3) & 3) << 2)) & (SPR - 1);
-  };
-  auto fv = [](int key) __attribute__((always_inline)) { return ((key & 3) << 1) & (SPR - 1); };
-
   const uint32_t lbase = lds_off(lds);
   const int nkb = min(qb + 1, (s + PF_KB - 1) / PF_KB);
   auto issue = [&](int kb, int st) __attribute__((always_inline)) {
@@ -461,9 +559,9 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
       const int slot = lane % SPR;
       const int row = min(kb * PF_KB + key, s - 1);
       const _Float16* src = base + (int64_t)row * ld;
-      dma16(src + a.h1 + 8 * (slot ^ fk(key)),
+      dma16(src + a.h1 + 8 * (slot ^ swz_k<SPR>(key)),
             __builtin_amdgcn_readfirstlane(lbase + st * STAGE + u * 1024));
-      dma16(src + 2 * a.h1 + 8 * (slot ^ fv(key)),
+      dma16(src + 2 * a.h1 + 8 * (slot ^ swz_v<SPR>(key)),
             __builtin_amdgcn_readfirstlane(lbase + st * STAGE + PF_KB * RB + u * 1024));
     }
   };
@@ -472,6 +570,7 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_lane = 0.f;
+  auto visible = [&](int kidx) __attribute__((always_inline)) { return kidx <= qi && kidx < s; };
 
   issue(0, 0);
   for (int kb = 0; kb < nkb; ++kb) {
@@ -480,89 +579,140 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
     __builtin_amdgcn_s_barrier();
     if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
     const uint8_t* Kl = lds + st * STAGE;
-    const uint8_t* Vl = Kl + PF_KB * RB;
-
-    // scores of 4 tiles of 16 keys; tile T row m holds key
-    // 32 (T / 2) + 8 (m / 4) + 4 (T % 2) + m % 4
-    f32x4 sc[4];
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      const int key = 32 * (T / 2) + 8 * (r16 / 4) + 4 * (T % 2) + (r16 % 4);
-      const uint8_t* kr = Kl + key * RB;
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const f16x8 kf = *(const f16x8*)(kr + 16 * ((G + 4 * ks) ^ fk(key)));
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], c, 0, 0, 0);
-      }
-      sc[T] = c;
-    }
-    // mask (causal and past the prompt), block maximum per query
-    float mx = -INFINITY;
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kidx = kb * PF_KB + 32 * (T / 2) + 8 * G + 4 * (T % 2) + e;
-        if (kidx > qi || kidx >= s) sc[T][e] = -INFINITY;
-        mx = fmaxf(mx, sc[T][e]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float mc = -m_use * c2;
-    const float alpha = __builtin_amdgcn_exp2f(fmaf(m_run, c2, mc));
-    m_run = m_new;
-    float ps = 0.f;
-    f16x8 pb[2];
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[T][e], c2, mc));
-        ps += p;
-        pb[T / 2][4 * (T % 2) + e] = (_Float16)p;
-      }
-    l_lane = fmaf(l_lane, alpha, ps);
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
-    // O^T += V^T P^T over two 32-key steps
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        f16x8 vf;
-#pragma unroll
-        for (int n2 = 0; n2 < 2; ++n2) {
-          const int row = 32 * p + 8 * G + 4 * n2 + r16 / 4;
-          const int d = 16 * db + 4 * (r16 % 4);
-          const uint8_t* vp = Vl + row * RB + 16 * ((d / 8) ^ fv(row)) + 2 * (d % 8);
-          const s16x4 t = ds_read_tr16(vp);
-          const f16x4 th = __builtin_bit_cast(f16x4, t);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vf[4 * n2 + e] = th[e];
-        }
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[p], o[db], 0, 0, 0);
-      }
-    }
+    flash_block<D>(Kl, Kl + PF_KB * RB, qf, kb * PF_KB, visible, c2, m_run, l_lane, o);
   }
   wait_vm<0>();
-  // the 4 lanes of a query hold complementary key subsets: total their sums
-  float l = l_lane + __shfl_xor(l_lane, 16);
-  l += __shfl_xor(l, 32);
-  if (qi >= s) return;
-  const float inv = 1.0f / l;
-  _Float16* op = a.out + ((int64_t)r * s + qi) * a.h1 + h * D + 4 * G;
+  flash_store<D>(qi < s ? a.out + ((int64_t)r * s + qi) * a.h1 + h * D : nullptr, l_lane, o);
+}
+
+// ------------------------------------------------ multi-query decode (int4)
+// q >= 16 new tokens per request over the int4 cache (tree decode of
+// [SpecPipe] 2.2.1, or chain decode): one workgroup per (request, head),
+// 4 waves of 16 queries.  Each 64-row block of the cache arrives in LDS by
+// direct loads (codes and scale/min pairs, double-buffered), is expanded once
+// into fp16 K and V tiles (fp16(c * scale + min), one rounding: the values
+// the oracle's dequantiser gives), and flash_block runs over the tiles with
+// the tree visibility: every prefix row, plus tree rows flagged in the
+// query's mask (or rows up to the query's own for a chain).
+template <int D>
+__global__ __launch_bounds__(256) void k_multi_attn(DecArgs a) {
+  constexpr int KS = D / 32, DB = D / 16, RB = 2 * D, SPR = RB / 16;
+  constexpr int CB = D / 2;           // code bytes per cache row
+  constexpr int NG = D / 64;          // groups per row
+  constexpr int CODES = 64 * CB;      // code bytes per block, per tensor
+  constexpr int SMB = 64 * 4 * NG;    // scale/min bytes per block, per tensor
+  constexpr int STG = 2 * CODES + 2 * SMB;
+  constexpr int NCI = CODES / 1024;   // 1 KB direct loads per tensor per block
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2 * 64 * RB];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[2 * STG];
+
+  const int lane = threadIdx.x & 63, r16 = lane & 15, G = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x % a.H, r = blockIdx.x / a.H;
+  const int P = a.pos + (a.dpos ? *a.dpos : 0);
+  const int R = P + a.q;
+  const int qi = 16 * wave + r16;
+  const int qrow = min(qi, a.q - 1);
+  const uint64_t mask = a.masks ? a.masks[(int64_t)r * a.q + qrow] : 0ull;
+  const float c2 = 1.44269504088896341f / sqrtf((float)D);
+  const int64_t rowbase = ((int64_t)r * a.H + h) * a.cap;
+  const uint8_t* kc = (const uint8_t*)a.k + rowbase * CB;
+  const uint8_t* vc = (const uint8_t*)a.v + rowbase * CB;
+  const uint8_t* ks_ = (const uint8_t*)(a.ksm + rowbase * NG);
+  const uint8_t* vs_ = (const uint8_t*)(a.vsm + rowbase * NG);
+
+  f16x8 qf[KS];
+  {
+    const _Float16* qp = a.qkv + ((int64_t)r * a.q + qrow) * 3 * a.h1 + h * D + 8 * G;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    f16x4 y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[db][e] * inv);
-    *(f16x4*)(op + 16 * db) = y;
+    for (int k = 0; k < KS; ++k) qf[k] = *(const f16x8*)(qp + 32 * k);
   }
+
+  const uint32_t sbase = lds_off(stage);
+  auto issue = [&](int kb, int st) __attribute__((always_inline)) {
+    const uint32_t sb = sbase + st * STG;
+    if (wave < NCI) {
+      // 1 KB of rows: lane l -> row (1024 / CB) wave + l / (CB / 16), 16-byte piece l % (CB / 16)
+      const int row = min(kb * 64 + (1024 / CB) * wave + lane / (CB / 16), R - 1);
+      const int off = row * CB + 16 * (lane % (CB / 16));
+      dma16(kc + off, __builtin_amdgcn_readfirstlane(sb + wave * 1024));
+      dma16(vc + off, __builtin_amdgcn_readfirstlane(sb + CODES + wave * 1024));
+    }
+    if (wave == 0 || wave == 1) {
+      // scale/min pairs of 64 rows (K by wave 0, V by wave 1): one (row,
+      // group) dword per lane, NG loads of 64 lanes
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int u = 64 * i + lane;
+        const int row = min(kb * 64 + u / NG, R - 1);
+        dma4((wave ? vs_ : ks_) + (row * NG + u % NG) * 4,
+             __builtin_amdgcn_readfirstlane(sb + 2 * CODES + wave * SMB + 256 * i));
+      }
+    }
+  };
+  // expansion of one 16-byte piece (32 codes of one row, one group) into fp16
+  // at its swizzled chunks: code pair (2p, 2p+1) of a dword = byte p's low and
+  // high nibbles, placed under the exponents of 1024 and 64 by one byte
+  // permute and one and-or, made exact by one packed subtraction, then one
+  // packed FMA with the row's scale and min
+  const uint32_t magic = in_vgpr(0x54006400u);
+  const f16x2 off = {(_Float16)-1024.0f, (_Float16)-64.0f};
+  auto expand = [&](const uint8_t* codes, uint32_t smw, uint8_t* dst_row, int piece, int swz)
+      __attribute__((always_inline)) {
+    const u32x4 w = *(const u32x4*)codes;
+    const f16x2 sm = h2_of(smw);
+    const f16x2 sc = {sm[0], sm[0]}, mn = {sm[1], sm[1]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 y;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t x = __builtin_amdgcn_perm(w[j], w[j], 0x0C000C00u | p | (p << 16));
+        const f16x2 c = h2_of((x & 0x00F0000Fu) | magic) + off;
+        y[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, sc, mn));
+      }
+      *(u32x4*)(dst_row + 16 * ((4 * piece + j) ^ swz)) = y;
+    }
+  };
+
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+  auto visible = [&](int kidx) __attribute__((always_inline)) {
+    const unsigned t = (unsigned)(kidx - P);
+    const bool tree = a.masks ? (bool)((mask >> (t & 63u)) & 1ull) : (int)t <= qi;
+    return kidx < R && (kidx < P || tree);
+  };
+
+  const int nkb = (R + 63) / 64;
+  issue(0, 0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int st = kb & 1;
+    wait_vm<0, 0>();
+    __builtin_amdgcn_s_barrier();  // staging kb landed; every wave is done with the tiles
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+    const uint8_t* sb = stage + st * STG;
+    // this wave expands rows 16 wave .. 16 wave + 15 of K and of V
+    constexpr int PPR = CB / 16;            // pieces per row
+    constexpr int UNITS = 2 * 16 * PPR;     // (tensor, row, piece) per wave
+#pragma unroll
+    for (int pass = 0; pass < UNITS / 64; ++pass) {
+      const int u = 64 * pass + lane;
+      const int tsr = u / (16 * PPR), rem = u % (16 * PPR);
+      const int row = 16 * wave + rem / PPR, piece = rem % PPR;
+      const uint8_t* codes = sb + tsr * CODES + row * CB + 16 * piece;
+      const uint32_t smw =
+          *(const uint32_t*)(sb + 2 * CODES + tsr * SMB + row * 4 * NG + 4 * ((32 * piece) / 64));
+      uint8_t* dst = tiles + tsr * 64 * RB + row * RB;
+      expand(codes, smw, dst, piece, tsr ? swz_v<SPR>(row) : swz_k<SPR>(row));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile writes are done
+    __builtin_amdgcn_s_barrier();
+    flash_block<D>(tiles, tiles + 64 * RB, qf, kb * 64, visible, c2, m_run, l_lane, o);
+  }
+  wait_vm<0>();
+  flash_store<D>(qi < a.q ? a.out + ((int64_t)r * a.q + qi) * a.h1 + h * D : nullptr, l_lane, o);
 }
 
 // ------------------------------------------------------------ tree masks
@@ -626,6 +776,15 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
             masks,                kv.cap, kv.k, kv.v,  (const uint32_t*)kv.k_sm,
             (const uint32_t*)kv.v_sm, (_Float16*)out};
   const int D = h1 / heads;
+  if (kv.fmt == HP_Q4 && q >= 16) {
+    Prof prof("attn_multi_q4", st);
+    const dim3 grid((unsigned)((int64_t)b * heads));
+    if (D == 128)
+      hipLaunchKernelGGL(k_multi_attn<128>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_multi_attn<64>, grid, dim3(256), 0, st, a);
+    return;
+  }
   const dim3 grid((unsigned)((int64_t)b * heads * q));
   Prof prof(kv.fmt == HP_Q4 ? "attn_decode_q4" : "attn_decode_f16", st);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, a); };

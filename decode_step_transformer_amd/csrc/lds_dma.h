@@ -22,6 +22,17 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
       : "memory", "m0");
 }
 
+// One 4-byte direct load per active lane into LDS at m0 + 4 * lane.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(g), "s"(lds_base)
+      : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(n) lgkmcnt(l) (gfx9 encoding; expcnt unconstrained).
 template <int n, int l = 15>
 __device__ __forceinline__ void wait_vm() {

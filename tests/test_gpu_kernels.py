@@ -165,7 +165,10 @@ def _cache_values(orc, kv, T):
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("P,q,tree", [(0, 1, False), (1, 1, False), (63, 1, False), (200, 1, False),
-                                      (70, 7, False), (130, 64, True), (0, 5, True)])
+                                      (70, 7, False), (130, 64, True), (0, 5, True),
+                                      # q >= 16: the multi-query MFMA path for int4 caches
+                                      (0, 16, True), (37, 16, False), (300, 33, True),
+                                      (129, 64, False), (1000, 20, True), (64, 48, True)])
 def test_decode_attention(hp, orc, fmt, D, P, q, tree):
     import torch
     b, heads = 3, 2
