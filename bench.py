@@ -17,6 +17,8 @@ Prints one JSON line (rank 0, N = 1 only):
                    published MI355X peak for its bound;
   decode_kernels-- the same for the decode-phase kernels (one eager decode
                    column after the timed region);
+  tree_attention-- the tree-masked decode attention workload (8 requests,
+                   2048-row int4 prefix, 64 tree tokens), event-timed;
   cpu_baseline  -- the CPU oracle timed on a bounded sample of the same
                    workload (one decode layer for a few requests).
 """
@@ -89,6 +91,55 @@ def setup(c, seed, hp, torch):
     return d, layers, x, t_in, kvs, ws, x_out, t_out
 
 
+TREE = dict(b=8, h1=8192, heads=64, prefix=2048, q=64)  # tree-masked decode attention workload
+
+
+def tree_attention(hp, torch, stream, reps=20):
+    """The tree-masked decode attention workload ([SpecPipe] 2.2.1 masks over an int4
+    cache): b requests, an int4 prefix of `prefix` rows, q tree tokens with random
+    BFS parent arrays; timed with HIP events over `reps` launches."""
+    t = TREE
+    b, h1, H, P, q = t["b"], t["h1"], t["heads"], t["prefix"], t["q"]
+    D = h1 // H
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    sig = 0.02 * h1 ** 0.5
+    kv = hp.KVCache(1, b, H, P + q, D)
+    pre = (torch.randn((b, P, 3 * h1), generator=g, device="cuda") * sig).half()
+    hp.hp_kv_append(b, P, h1, H, pre, 0, kv, stream=stream)
+    del pre
+    qkv = (torch.randn((b, q, 3 * h1), generator=g, device="cuda") * sig).half()
+    hp.hp_kv_append(b, q, h1, H, qkv, P, kv, stream=stream)
+    # random breadth-first trees: parent[i] = min(parent[i-1] + bit, i - 1)
+    bits = torch.randint(0, 2, (b, q), generator=g, device="cuda")
+    parent = torch.full((b, q), -1, dtype=torch.int32)
+    bh = bits.cpu()
+    for r in range(b):
+        if q > 1:
+            parent[r, 1] = 0
+        for i in range(2, q):
+            parent[r, i] = min(int(parent[r, i - 1]) + int(bh[r, i]), i - 1)
+    masks, err = hp.hp_tree_masks(parent.cuda(), stream=stream)
+    out = torch.empty((b, q, h1), dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        hp.hp_decode_attention(b, q, h1, H, qkv, P, kv, masks=masks, out=out, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        hp.hp_decode_attention(b, q, h1, H, qkv, P, kv, masks=masks, out=out, stream=stream)
+    e1.record(stream)
+    stream.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    cache_bytes = 2.0 * b * H * (P + q) * (D / 2 + 4 * D / 64)
+    flops = 4.0 * D * b * H * q * P                       # prefix part; tree rows add < 2%
+    return {"workload": f"tree-masked decode attention b={b} h1={h1} heads={H} prefix={P} q={q} "
+                        "int4 cache",
+            "avg_us": ms * 1e3, "bound": "hbm", "gbs": cache_bytes / (ms / 1e3) / 1e9,
+            "frac_hbm": cache_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "tflops": flops / (ms / 1e3) / 1e12,
+            "work": "cache bytes 2*b*heads*(prefix+q)*(d/2 + 4*d/64) per launch, one read"}
+
+
 def cpu_baseline(c, cname, seconds_hint=20.0):
     """The oracle (as it stands) on one decode layer for a few requests."""
     import numpy as np
@@ -139,6 +190,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="opt-30b-int4", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tree", action="store_true", help="skip the tree-attention workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; each GPU would run its own block "
@@ -192,6 +244,7 @@ def main():
         stream.synchronize()
         hp.hp_profile(False)
         dprof = hp.hp_profile_read()
+        tree = None if args.no_tree else tree_attention(hp, torch, stream)
     nonfinite = int((~torch.isfinite(t_out.float())).sum().item())
 
     b, n, s, l = c["b"], c["n"], c["s"], c["l"]
@@ -258,6 +311,7 @@ def main():
         "nonfinite_decode_outputs": nonfinite,
         "roofline": roof,
         "decode_kernels": dec,
+        "tree_attention": tree,
         "kernels": {k: {"launches": v[0], "total_ms": v[1]} for k, v in prof.items()},
     }
     if not args.no_cpu_baseline:
