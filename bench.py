@@ -60,6 +60,16 @@ def weight_bytes_per_layer(c):
     return elems * (0.5 + 4 / 64) if c["fmt"] == 1 else elems * 2.0
 
 
+def gemm_min_bytes(c, M):
+    """Bytes per prefill GEMM launch if every operand moved once (fp16 activations
+    and expanded weights read, output and residual), averaged over the layer's
+    four products (QKV, output projection with residual, W1, W2 with residual)."""
+    h1, h2 = c["h1"], c["h2"]
+    prods = ((h1, 3 * h1, 0), (h1, h1, 1), (h1, h2, 0), (h2, h1, 1))
+    tot = sum(2.0 * (M * k + k * n + M * n * (1 + r)) for k, n, r in prods)
+    return tot / len(prods)
+
+
 def kv_bytes_read(c, T):
     """Cache bytes one decode attention launch must read: K and V rows [0, T)."""
     per_row = c["h1"] * (0.5 + 4 / 64) if c["fmt"] == 1 else c["h1"] * 2.0
@@ -257,12 +267,16 @@ def main():
     dom = max(prof.items(), key=lambda kv: kv[1][1])
     name, (launches, tot_ms) = dom
     M = b * s
+    from decode_step_transformer_amd import traffic as tr
     if name.startswith("gemm_") and name.endswith("_tiled"):
         algo = K * l * layer_flops(c, M) / 1e12      # TFLOP over the timed region
         achieved = algo / (tot_ms / 1e3)
         roof = {"kernel": name, "bound": "mfma", "achieved": achieved,
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS,
+                "traffic": tr.lookup("k_gemm16", args.config) if name == "gemm_f16_tiled" else None,
+                "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+                "traffic_min": gemm_min_bytes(c, M) if name == "gemm_f16_tiled" else None,
                 "launches": launches, "avg_launch_ms": tot_ms / launches,
                 "work": "2*M*(4*h1^2 + 2*h1*h2) flops per layer, M = b*s"}
     else:
@@ -272,8 +286,11 @@ def main():
 
     # decode-phase kernels
     dec = {}
+    dec_kernel = {"gemm_q4_skinny": "k_gemm_dq", "attn_decode_q4": "k_decode_attn"}
     for kname, (cnt, ms) in dprof.items():
         e = {"launches": cnt, "avg_launch_ms": ms / cnt, "total_ms": ms}
+        if kname in dec_kernel:
+            e["traffic"] = tr.lookup(dec_kernel[kname], args.config)
         if kname.startswith("gemm_") and kname.endswith("_skinny"):
             fl = l * layer_flops(c, b) / 1e12
             by = l * weight_bytes_per_layer(c) / 1e9
