@@ -9,19 +9,16 @@
 //    16-column subtiles, for all BM rows.
 //  * The activation tile x[BM][128] of each k-block is staged through LDS
 //    (double-buffered, rows padded by 16 B) and shared by the 4 waves.
-//  * Weight fragments go straight from HBM to registers: in the packed
-//    layout one 16-column subtile of one 128-deep k-block is 1 KB, 16 B per
-//    lane, already in MFMA fragment order; int4 codes are expanded with the
-//    1024-offset binary16 trick and one packed FMA with the group's scale and
-//    min (a single rounding, the same value the oracle's dequantiser gives).
+//  * Weight fragments (fp16, wt[n][k] rows) go straight from HBM to
+//    registers, four 16-byte chunks per lane and subtile per k-block.
 //  * MFMA operand A is the weight fragment (16 output columns), operand B the
 //    activation fragment (16 rows), so each lane ends with 4 consecutive
 //    output columns of one row: 8-byte stores.
 //  * Skinny products (M <= 144, the decode step) split k over workgroups;
 //    partial sums go to fp32 scratch and a second kernel adds them in split
-//    order, so the result depends only on (k, n), never on M.  int4 weights
-//    with more than 16 rows use the 8-wave kernel of gemm_dec.hip instead
-//    of the 4-wave kernel here.
+//    order, so the result depends only on (k, n), never on M.  Skinny int4
+//    products run on the 8-wave kernel of gemm_dec.hip (same split rule);
+//    tall ones expand int4 weights to fp16 and run k_gemm16.
 #include <type_traits>
 
 #include "common.h"
@@ -47,20 +44,17 @@ __device__ __forceinline__ void unroll(F&& f) {
 struct GemmArgs {
   const _Float16* A;
   int64_t lda, M;
-  const void* B;
-  const _Float16* scale;
-  const _Float16* minv;
+  const _Float16* B;  // wt[N][K]
   int K, N, splits, mtiles;  // split s covers k-blocks [s KB / splits, (s+1) KB / splits)
   const _Float16* res;
   int64_t ldr;
-  DqConst dq;
   int relu;
   _Float16* Y;
   int64_t ldy;
   float* P;  // split partials [split][M][N] or null
 };
 
-constexpr int NS = 3;  // LDS stages (activations, scales) and weight register slots
+constexpr int NS = 3;  // LDS activation stages and weight register slots
 
 // Workgroup tile order: workgroups on the same XCD (id % 8) take a contiguous
 // run of tiles, and runs sweep 4 row tiles at a time so that concurrently
@@ -82,20 +76,17 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, int& mt, int& nt) {
 // One wave's part of a workgroup tile: TM 16-row tiles starting at row tile
 // rt0 of the workgroup's rows (from m0), times the 64 output columns of wave
 // column wcol.  All NT threads of the workgroup stage SR activation rows per
-// k-block into As (NS stages of SR x LDS_ROW halves); Ssm holds this wave's
-// int4 group scales/mins (NS stages of 64 dwords of scale pairs, then 64 of
-// min pairs).
-template <int TM, bool Q4, int NT, int SR>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, uint32_t* Ssm_,
-                                          int tid, int wcol, int rt0, int64_t m0, int nt) {
+// k-block into As (NS stages of SR x LDS_ROW halves).
+template <int TM, int NT, int SR>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int tid, int wcol,
+                                          int rt0, int64_t m0, int nt) {
   const int lane = tid & 63;
   const int KB = g.K / BK;
   auto As = [&](int stage) __attribute__((always_inline)) { return As_ + stage * (SR * LDS_ROW); };
-  auto Ssm = [&](int stage) __attribute__((always_inline)) { return Ssm_ + stage * 128; };
   const int n_wave = nt * 256 + wcol * 64;
   const bool wave_on = n_wave < g.N;
   // a wave past the last column reloads the last group (never stored), so
-  // every load is unconditional and wait counts stay static
+  // every load is unconditional
   const int n_ld = min(n_wave, g.N - 64);
   const int split = blockIdx.y;
   const int kb0 = split * KB / g.splits, kb1 = (split + 1) * KB / g.splits;
@@ -127,39 +118,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, uint
   // ---- weight fragments ----
   const int kq = lane >> 4, r16 = lane & 15;
   struct Raw {
-    u32x4 c[Q4 ? 4 : 16];  // Q4: codes per subtile; F16: 4 chunks per subtile
+    u32x4 c[16];  // 4 chunks per subtile
   };
-  const u32x4* Bq = (const u32x4*)g.B + ((int64_t)(n_ld >> 4) * KB) * 64 + lane;
-  const _Float16* Bh = (const _Float16*)g.B + (int64_t)(n_ld + r16) * g.K + 32 * kq;
+  const _Float16* Bh = g.B + (int64_t)(n_ld + r16) * g.K + 32 * kq;
   auto load_b = [&](Raw& R, int kb) __attribute__((always_inline)) {
-    if constexpr (Q4) {
-      unroll<4>([&](auto t_) {
-        constexpr int t = decltype(t_)::value;
-        R.c[t] = Bq[((int64_t)t * KB + kb) * 64];
+    unroll<4>([&](auto t_) {
+      constexpr int t = decltype(t_)::value;
+      const u32x4* p = (const u32x4*)(Bh + (int64_t)16 * t * g.K + (int64_t)kb * BK);
+      unroll<4>([&](auto j_) {
+        constexpr int j = decltype(j_)::value;
+        R.c[4 * t + j] = p[j];
       });
-    } else {
-      unroll<4>([&](auto t_) {
-        constexpr int t = decltype(t_)::value;
-        const u32x4* p = (const u32x4*)(Bh + (int64_t)16 * t * g.K + (int64_t)kb * BK);
-        unroll<4>([&](auto j_) {
-          constexpr int j = decltype(j_)::value;
-          R.c[4 * t + j] = p[j];
-        });
-      });
-    }
-  };
-  // scale/min of this wave's group for one k-block: lanes 0-31 fetch scale
-  // pairs, lanes 32-63 min pairs, 8 bytes each
-  const _Float16* smsrc = (lane < 32 ? g.scale : g.minv) + (int64_t)(n_ld >> 6) * g.K + 4 * (lane & 31);
-  u32x2 sreg;
-  auto load_sm = [&](int kb) __attribute__((always_inline)) {
-    if constexpr (Q4) sreg = *(const u32x2*)(smsrc + (int64_t)kb * BK);
-  };
-  auto store_sm = [&](int stage) __attribute__((always_inline)) {
-    if constexpr (Q4) *(u32x2*)(Ssm(stage) + 2 * lane) = sreg;
+    });
   };
 
-  const DqConst dq{g.dq.mask0, g.dq.mask1, in_vgpr(g.dq.magic0), in_vgpr(g.dq.magic1)};
   f32x4 acc[TM][4];
   unroll<TM>([&](auto i_) {
     unroll<4>([&](auto t_) { acc[decltype(i_)::value][decltype(t_)::value] = f32x4{0.f, 0.f, 0.f, 0.f}; });
@@ -174,22 +146,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, uint
       x[i] = *(const f16x8*)(Ab + 16 * i * LDS_ROW);
     });
   };
-  auto make_w = [&](f16x8 (&w)[4], const Raw& R, int stage, auto j_) __attribute__((always_inline)) {
+  auto make_w = [&](f16x8 (&w)[4], const Raw& R, auto j_) __attribute__((always_inline)) {
     constexpr int j = decltype(j_)::value;
-    if constexpr (Q4) {
-      const uint32_t* Sb = Ssm(stage) + 16 * kq + 4 * j;
-      const u32x4 sv = *(const u32x4*)Sb;
-      const u32x4 mv = *(const u32x4*)(Sb + 64);
-      unroll<4>([&](auto t_) {
-        constexpr int t = decltype(t_)::value;
-        w[t] = dequant8(R.c[t][j], sv, mv, dq);
-      });
-    } else {
-      unroll<4>([&](auto t_) {
-        constexpr int t = decltype(t_)::value;
-        w[t] = as_f16x8(R.c[4 * t + j]);
-      });
-    }
+    unroll<4>([&](auto t_) {
+      constexpr int t = decltype(t_)::value;
+      w[t] = as_f16x8(R.c[4 * t + j]);
+    });
   };
   auto mma = [&](const f16x8 (&w)[4], const f16x8 (&x)[TM]) __attribute__((always_inline)) {
     unroll<TM>([&](auto i_) {
@@ -201,7 +163,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, uint
     });
   };
   // issue order inside one k-step: the LDS reads of the next step first,
-  // then each MFMA followed by two VALU instructions (the next dequant)
+  // then each MFMA followed by two VALU instructions
   auto interleave = [&]() __attribute__((always_inline)) {
     unroll<TM + 2>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
     unroll<4 * TM>([&](auto) {
@@ -211,23 +173,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, uint
   };
 
   Raw r0, r1, r2;
-  // prologue: stages 0 and 1 hold activation/scale blocks kb0 and kb0+1;
-  // weight slots 0 and 1 hold kb0 and kb0+1; registers hold block kb0+2
+  // prologue: stages 0 and 1 hold activation blocks kb0 and kb0+1; weight
+  // slots 0 and 1 hold kb0 and kb0+1; registers hold block kb0+2
   load_a(kb0);
-  load_sm(kb0);
   load_b(r0, kb0);
   load_b(r1, clampk(kb0 + 1));
   store_a(0);
-  store_sm(0);
   load_a(clampk(kb0 + 1));
-  load_sm(clampk(kb0 + 1));
   store_a(1);
-  store_sm(1);
   load_a(clampk(kb0 + 2));
-  load_sm(clampk(kb0 + 2));
   __syncthreads();
   read_x(xa, 0, 0);
-  make_w(wa, r0, 0, std::integral_constant<int, 0>());
+  make_w(wa, r0, std::integral_constant<int, 0>());
 
   // k-block kb in stage st % 3, weights in `cur`; `nxt` holds kb+1, `fill`
   // receives kb+2.  At entry xa/wa hold the fragments of (kb, j = 0).
@@ -235,29 +192,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, uint
     const int st = (kb - kb0) % NS, st1 = (kb - kb0 + 1) % NS, st2 = (kb - kb0 + 2) % NS;
     __syncthreads();  // every wave is done with stage st2 (block kb-1)
     store_a(st2);
-    store_sm(st2);
     load_a(clampk(kb + 3));
-    load_sm(clampk(kb + 3));
     load_b(fill, clampk(kb + 2));
     __builtin_amdgcn_sched_barrier(0);
     read_x(xb, st, 1);
     mma(wa, xa);
-    make_w(wb, cur, st, std::integral_constant<int, 1>());
+    make_w(wb, cur, std::integral_constant<int, 1>());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
     read_x(xa, st, 2);
     mma(wb, xb);
-    make_w(wa, cur, st, std::integral_constant<int, 2>());
+    make_w(wa, cur, std::integral_constant<int, 2>());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
     read_x(xb, st, 3);
     mma(wa, xa);
-    make_w(wb, cur, st, std::integral_constant<int, 3>());
+    make_w(wb, cur, std::integral_constant<int, 3>());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
     read_x(xa, st1, 0);
     mma(wb, xb);
-    make_w(wa, nxt, st1, std::integral_constant<int, 0>());
+    make_w(wa, nxt, std::integral_constant<int, 0>());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -305,15 +260,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, uint
 
 // Products with one row tile per workgroup (or any M): 4 waves, each with all
 // TM row tiles of its 64 columns.
-template <int TM, bool Q4>
+template <int TM>
 __global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) _Float16 As[NS * 16 * TM * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint32_t Ssm[4][NS * 128];
   int mt, nt;
   tile_of(g, mt, nt);
   const int wave = threadIdx.x >> 6;
-  gemm_tile<TM, Q4, 256, 16 * TM>(g, As, Ssm[wave], threadIdx.x, wave, 0, (int64_t)mt * 16 * TM,
-                                  nt);
+  gemm_tile<TM, 256, 16 * TM>(g, As, threadIdx.x, wave, 0, (int64_t)mt * 16 * TM, nt);
 }
 
 // Sums split-k partials in split order, then applies the epilogue.
@@ -382,74 +335,62 @@ static int split_for(int32_t k, int32_t n) {
 size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {
   if (M <= 0) return 0;
   if (M > SKINNY_M) return fmt == HP_Q4 ? (size_t)k * (size_t)n * 2 : 0;  // fp16 expansion
-  const int s = (fmt == HP_Q4 && M > 16) ? split_rs(k, n) : split_for(k, n);
+  const int s = fmt == HP_Q4 ? split_rs(k, n) : split_for(k, n);
   return s > 1 ? (size_t)s * (size_t)M * (size_t)n * sizeof(float) : 0;
 }
 
 template <int TM>
-static void launch_tm(const GemmArgs& a, bool q4, dim3 grid, hipStream_t st) {
-  const bool skinny = a.mtiles == 1 && a.M <= SKINNY_M;
-  Prof prof(q4 ? (skinny ? "gemm_q4_skinny" : "gemm_q4_tiled")
-               : (skinny ? "gemm_f16_skinny" : "gemm_f16_tiled"), st);
-  if (q4)
-    hipLaunchKernelGGL((k_gemm<TM, true>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_gemm<TM, false>), grid, dim3(256), 0, st, a);
+static void launch_tm(const GemmArgs& a, dim3 grid, hipStream_t st) {
+  Prof prof("gemm_f16_skinny", st);
+  hipLaunchKernelGGL(k_gemm<TM>, grid, dim3(256), 0, st, a);
 }
 
 hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, const void* res,
                       int64_t ldr, bool relu, void* y, int64_t ldy, void* ws, hipStream_t st) {
   if (M == 0) return HP_OK;
-  GemmArgs a;
-  a.A = (const _Float16*)x;
-  a.lda = ldx;
-  a.M = M;
-  a.B = w.data;
-  a.scale = (const _Float16*)w.scale;
-  a.minv = (const _Float16*)w.minv;
-  a.K = w.k;
-  a.N = w.n;
-  a.res = (const _Float16*)res;
-  a.ldr = ldr;
-  a.relu = relu ? 1 : 0;
-  a.Y = (_Float16*)y;
-  a.ldy = ldy;
-  a.P = nullptr;
-  a.dq = DqConst{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
   const bool q4 = w.fmt == HP_Q4;
-  const int KB = w.k / BK;
-  const int ntiles = (int)cdiv(w.n, 256);
   if (M <= SKINNY_M) {
-    const int TM = (int)cdiv(M, 16);
-    const bool rs = q4 && TM >= 2;
-    const int splits = rs ? split_rs(w.k, w.n) : split_for(w.k, w.n);
-    a.splits = splits;
-    a.mtiles = 1;
-    if (splits > 1) a.P = (float*)ws;
-    const dim3 grid(ntiles, splits);
-    if (rs) {
+    const int splits = q4 ? split_rs(w.k, w.n) : split_for(w.k, w.n);
+    if (q4) {
       hp_status s = launch_gemm_dq(x, ldx, w, M, res, ldr, relu, y, ldy, splits, (float*)ws, st);
       if (s != HP_OK) return s;
     } else {
-      switch (TM) {
-        case 1: launch_tm<1>(a, q4, grid, st); break;
-        case 2: launch_tm<2>(a, q4, grid, st); break;
-        case 3: launch_tm<3>(a, q4, grid, st); break;
-        case 4: launch_tm<4>(a, q4, grid, st); break;
-        case 5: launch_tm<5>(a, q4, grid, st); break;
-        case 6: launch_tm<6>(a, q4, grid, st); break;
-        case 7: launch_tm<7>(a, q4, grid, st); break;
-        case 8: launch_tm<8>(a, q4, grid, st); break;
-        default: launch_tm<9>(a, q4, grid, st); break;
+      GemmArgs a;
+      a.A = (const _Float16*)x;
+      a.lda = ldx;
+      a.M = M;
+      a.B = (const _Float16*)w.data;
+      a.K = w.k;
+      a.N = w.n;
+      a.res = (const _Float16*)res;
+      a.ldr = ldr;
+      a.relu = relu ? 1 : 0;
+      a.Y = (_Float16*)y;
+      a.ldy = ldy;
+      a.splits = splits;
+      a.mtiles = 1;
+      a.P = splits > 1 ? (float*)ws : nullptr;
+      const dim3 grid((unsigned)cdiv(w.n, 256), splits);
+      switch ((int)cdiv(M, 16)) {
+        case 1: launch_tm<1>(a, grid, st); break;
+        case 2: launch_tm<2>(a, grid, st); break;
+        case 3: launch_tm<3>(a, grid, st); break;
+        case 4: launch_tm<4>(a, grid, st); break;
+        case 5: launch_tm<5>(a, grid, st); break;
+        case 6: launch_tm<6>(a, grid, st); break;
+        case 7: launch_tm<7>(a, grid, st); break;
+        case 8: launch_tm<8>(a, grid, st); break;
+        default: launch_tm<9>(a, grid, st); break;
       }
+      hp_status s = launch_ok("k_gemm");
+      if (s != HP_OK) return s;
     }
-    hp_status s = launch_ok("k_gemm");
-    if (s != HP_OK || splits == 1) return s;
+    if (splits == 1) return HP_OK;
     const int64_t quads = M * (w.n / 4);
     const int blocks = (int)std::min<int64_t>(cdiv(quads, 256), 8192);
     Prof prof("gemm_splitk_reduce", st);
     hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, st, (const float*)ws, splits,
-                       M, w.n, (const _Float16*)res, ldr, a.relu, (_Float16*)y, ldy);
+                       M, w.n, (const _Float16*)res, ldr, relu ? 1 : 0, (_Float16*)y, ldy);
     return launch_ok("k_splitk_reduce");
   }
   // tall products: fp16 MFMA kernel over LDS tiles; int4 weights are first

@@ -1,23 +1,28 @@
-// Skinny int4 products of the decode step: y = act(x·w) + res with x of at
-// most 144 rows and w in the packed group-wise int4 layout ([FlexGen] paper
+// Skinny int4 products of the decode step: y = act(x·w) + res with x of 1 to
+// 144 rows and w in the packed group-wise int4 layout ([FlexGen] paper
 // notes, section 5: int4 weights in groups of 64 along the output channels,
 // converted back to FP16 right before the product; background section: the
 // projections and MLP products are x·w).
 //
 // Design (gfx950, v_mfma_f32_16x16x32_f16, one 512-thread workgroup per CU):
-//  * The workgroup owns 256 output columns for one k-range (split-K); its 8
-//    waves are 4 column groups (64 columns = one int4 group, 4 subtiles of
-//    16) times 2 row halves, so two waves share every SIMD and one wave's
-//    MFMAs overlap the other's dequantisation.
+//  * The workgroup owns 256 output columns for one k-range (split-K).  Its
+//    8 waves are 4 column groups (64 columns = one int4 group, 4 subtiles
+//    of 16) times 2 k-step halves: the two waves on a SIMD (w and w + 4)
+//    hold all row tiles of the same 64 columns, wave w takes k-steps 0, 1 of
+//    each 128-deep k-block and wave w + 4 k-steps 2, 3.  Every weight element
+//    is expanded once per workgroup, and each activation fragment read from
+//    LDS feeds 4 MFMAs.  The two partial sums are added through LDS at the
+//    end (a fixed order).
 //  * Activations, packed codes and group scales/mins all reach LDS through
 //    direct loads (global_load_lds, no registers): activations in 2 stages
-//    (double-buffered, L2-resident), codes and scales in 4 stages, so weight
-//    bytes are requested 3 k-blocks before use.  Waits are explicit vmcnt
-//    counts: in every k-block each wave issues the next activation block
-//    first and then the weight block three ahead, so waiting for the
-//    activations leaves the last weight block in flight.
-//  * Activation rows are 256 B with 16-byte chunks XOR-swizzled by row, so
-//    the fragment reads of 16 consecutive rows hit distinct banks.
+//    (L2-resident), codes and scales in 4 stages, so weight bytes are
+//    requested 3 k-blocks before use.  Waits are explicit vmcnt counts.
+//  * LDS is the scarce resource (every byte of activations is read by four
+//    waves), so the per-block reads are kept to one 8-byte read of codes per
+//    subtile and one dword of scales/mins per lane; the 8 scale and 8 min
+//    pairs a lane needs per k-step come from the lanes of its row of 16 by
+//    DPP broadcast.  Activation rows are 256 B with 16-byte chunks XOR-
+//    swizzled by row (fragment reads of 16 rows hit distinct banks).
 //  * Codes are expanded in registers with the magic-exponent trick and one
 //    packed FMA with scale and min (a single rounding).
 //  * Split partials go to fp32 scratch, summed in split order by
@@ -32,10 +37,11 @@ namespace hp {
 
 namespace {
 
-constexpr int XS = 2;               // activation stages
-constexpr int WS = 4;               // code / scale stages
-constexpr int WBYTES = 16 * 1024;   // 16 subtiles x (64 lanes x 16 B)
-constexpr int SBYTES = 4 * 512;     // 4 groups x (128 scale + 128 min halves)
+constexpr int XS = 2;              // activation stages
+constexpr int WS = 4;              // code / scale stages
+constexpr int WBYTES = 16 * 1024;  // 16 subtiles x (64 lanes x 16 B)
+constexpr int SCH = 288;           // one scale or min chunk (128 halves), padded
+constexpr int SBYTES = 8 * SCH;    // 4 groups x (scale chunk, min chunk)
 
 template <int N, class F>
 __device__ __forceinline__ void unr(F&& f) {
@@ -60,13 +66,34 @@ struct DqArgs {
   float* P;  // split partials [split][M][N] or null
 };
 
-// One wave: row tiles [rt0, rt0 + TM) of the staged SR rows, 64 columns of
-// column group wcol.
-template <int TM, int SR>
-__device__ __forceinline__ void dq_wave(const DqArgs& g, uint8_t* lds, int wave, int wcol, int rt0,
-                                        int nt, int split) {
-  constexpr int XB = SR * 256;  // bytes per activation stage
-  constexpr int NX = SR / 32;   // activation loads per wave per k-block
+// Lane n of each row of 16 lanes, to every lane of that row.
+template <int n>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + n, 0xF, 0xF, false);
+}
+
+// One wave: column group wave & 3, all TM row tiles, k-steps 2 PH and
+// 2 PH + 1 of every k-block.
+//
+// Per wave the pipeline runs over its own steps (two per k-block): at the
+// start of a step the wave holds the step's activations and expanded
+// weights; during the step's MFMAs it expands the next step's weights and,
+// after the 4 MFMAs of each row tile, reads that tile's activations of the
+// next step into the registers just released.  Codes and scales of both of
+// the wave's steps of a block are read once, in its second step of the
+// previous block (after the k-block barrier that wave passes at the start of
+// that step, when its activations of the block are in registers: direct
+// loads of the next block have landed; the activations two blocks ahead and
+// the weights three blocks ahead are issued).
+template <int TM, int PH>
+__device__ __forceinline__ void dq_pair(const DqArgs& g, uint8_t* lds, int wave, int nt,
+                                        int split) {
+  constexpr int SR = 16 * TM;                          // staged rows
+  constexpr int XB = SR * 256;                         // bytes per activation stage
+  constexpr int NX = PH == 0 ? (TM + 1) / 2 : TM / 2;  // activation loads per block
+  constexpr int NWS = 3;  // code (2) and scale-or-min (1) loads per block
+  constexpr int J0 = 2 * PH;
+  const int wcol = wave & 3;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, kq = lane >> 4;
   const int KB = g.K / 128;
@@ -77,212 +104,203 @@ __device__ __forceinline__ void dq_wave(const DqArgs& g, uint8_t* lds, int wave,
   uint8_t* Sl = Wl + WS * WBYTES;
   const uint32_t xbase = lds_off(Xl), wbase = lds_off(Wl), sbase = lds_off(Sl);
 
-  // ---- direct-load sources of this lane ----
-  // activations: load p covers rows 32 p + 4 wave + (lane >> 4); LDS slot
-  // (lane & 15) of a row holds chunk slot ^ (row & 15).  Rows past M reload
-  // row M-1 (never stored).
-  const _Float16* xsrc[NX];
-  unr<NX>([&](auto p_) {
-    constexpr int p = decltype(p_)::value;
-    const int row = 32 * p + 4 * wave + (lane >> 4);
-    const int c = (lane & 15) ^ (row & 15);
-    xsrc[p] = g.A + (int64_t)min(row, g.M - 1) * g.lda + 8 * c;
-  });
-  // codes: subtiles 2 wave and 2 wave + 1 of the workgroup's 16 (columns
-  // past N reload the last subtile, never stored)
-  const uint8_t* wsrc[2];
-  unr<2>([&](auto h_) {
-    constexpr int h = decltype(h_)::value;
-    const int n16 = min(nt * 16 + 2 * wave + h, g.N / 16 - 1);
-    wsrc[h] = g.B + ((int64_t)n16 * KB * 64 + lane) * 16;
-  });
-  // scales (even waves) or mins (odd waves) of group wave >> 1, lanes 0-15
+  // ---- direct loads: wave-uniform base (SGPRs) + per-lane byte offset.
+  // Activations: load p covers rows 32 p + 4 wave + (lane >> 4) (waves
+  // 0-3 take one more load when TM is odd), slot (lane & 15) of a row
+  // holding chunk slot ^ (row & 15); rows past M (last load only) reload row
+  // M-1, never stored.  Codes: subtiles 2 wave, 2 wave + 1 of 16 (past N: the
+  // last one).  Chunk `wave` of the 8 scale / min chunks: the scales (even)
+  // or mins (odd) of group wave >> 1.
+  const int r0 = 4 * wave + (lane >> 4);
+  const int cx = (lane & 15) ^ (r0 & 15);
+  const uint32_t xoff = (uint32_t)(r0 * g.lda + 8 * cx) * 2u;
+  const uint32_t xoff_last =
+      (uint32_t)((min(32 * (NX - 1) + r0, g.M - 1) - 32 * (NX - 1)) * g.lda + 8 * cx) * 2u;
+  const uint32_t coff = (uint32_t)lane * 16u, soff = (uint32_t)lane * 4u;
   const int gi = min(nt * 4 + (wave >> 1), g.N / 64 - 1);
-  const _Float16* ssrc = ((wave & 1) ? g.minv : g.scale) + (int64_t)gi * g.K + 8 * (lane & 15);
-
+  const _Float16* sbase_g = ((wave & 1) ? g.minv : g.scale) + (int64_t)gi * g.K;
   auto blk = [&](int i) __attribute__((always_inline)) { return kb0 + min(i, nb - 1); };
   auto issue_x = [&](int i) __attribute__((always_inline)) {
     const int kb = blk(i);
     const uint32_t base = xbase + (i & 1) * XB + wave * 1024;
     unr<NX>([&](auto p_) {
       constexpr int p = decltype(p_)::value;
-      dma16(xsrc[p] + kb * 128, __builtin_amdgcn_readfirstlane(base + p * 8192));
+      dma16s(g.A + (int64_t)(32 * p) * g.lda + kb * 128, p == NX - 1 ? xoff_last : xoff,
+             __builtin_amdgcn_readfirstlane(base + p * 8192));
     });
   };
   auto issue_ws = [&](int i) __attribute__((always_inline)) {
     const int kb = blk(i);
     const uint32_t wb = wbase + (i & 3) * WBYTES + 2 * wave * 1024;
-    dma16(wsrc[0] + (int64_t)kb * 1024, __builtin_amdgcn_readfirstlane(wb));
-    dma16(wsrc[1] + (int64_t)kb * 1024, __builtin_amdgcn_readfirstlane(wb + 1024));
-    const uint32_t sb = sbase + (i & 3) * SBYTES + (wave >> 1) * 512 + (wave & 1) * 256;
-    if (lane < 16) dma16(ssrc + kb * 128, __builtin_amdgcn_readfirstlane(sb));
+    unr<2>([&](auto h_) {
+      constexpr int h = decltype(h_)::value;
+      const int n16 = min(nt * 16 + 2 * wave + h, g.N / 16 - 1);
+      dma16s(g.B + ((int64_t)n16 * KB + kb) * 1024, coff,
+             __builtin_amdgcn_readfirstlane(wb + h * 1024));
+    });
+    dma4s(sbase_g + kb * 128, soff,
+          __builtin_amdgcn_readfirstlane(sbase + (i & 3) * SBYTES + wave * SCH));
   };
 
-  // ---- fragments ----
   const DqConst dq{0x000F000Fu, 0x00F000F0u, in_vgpr(0x64006400u), in_vgpr(0x54005400u)};
   f32x4 acc[TM][4];
   unr<TM>([&](auto i_) {
     unr<4>([&](auto t_) { acc[decltype(i_)::value][decltype(t_)::value] = f32x4{0.f, 0.f, 0.f, 0.f}; });
   });
-  // Operands of the expansion: the 4 subtiles' codes of a whole k-block
-  // (one 16-byte read each, read during the previous block) and per k-step
-  // scale/min pairs (read one k-step ahead); activation fragments are read
-  // one k-step before their MFMAs.  Buffers alternate with the parity of the
-  // k-step (scales, fragments) and of the k-block (codes).
-  struct SM {
-    u32x4 sv, mv;
-  };
-  SM sa, sb;
-  u32x4 ca[4], cb[4];
-  f16x8 xa[TM], xb[TM], wa[4], wb[4];
-  // k-step j of a k-block: lane quarter kq contributes k = 32 kq + 8 j .. +7
-  auto read_x = [&](f16x8 (&x)[TM], int xs, int j) __attribute__((always_inline)) {
-    const uint8_t* base = Xl + xs * XB + (16 * rt0 + r16) * 256 + 16 * ((4 * kq + j) ^ r16);
-    unr<TM>([&](auto i_) {
-      constexpr int i = decltype(i_)::value;
-      x[i] = *(const f16x8*)(base + i * 16 * 256);
-    });
-  };
-  auto read_s = [&](SM& o, int wsg, int j) __attribute__((always_inline)) {
-    const uint8_t* sp = Sl + wsg * SBYTES + wcol * 512 + 64 * kq + 16 * j;
-    o.sv = *(const u32x4*)sp;
-    o.mv = *(const u32x4*)(sp + 256);
-  };
-  auto read_c = [&](u32x4 (&c)[4], int wsg) __attribute__((always_inline)) {
-    const uint8_t* cp = Wl + wsg * WBYTES + 4 * wcol * 1024 + lane * 16;
-    unr<4>([&](auto t_) {
-      constexpr int t = decltype(t_)::value;
-      c[t] = *(const u32x4*)(cp + t * 1024);
-    });
-  };
-  auto make_w = [&](f16x8 (&w)[4], const u32x4 (&c)[4], const SM& o, auto j_)
-      __attribute__((always_inline)) {
+  f16x8 x[TM], w[4];
+  uint32_t c0[4], c1[4];  // codes of the wave's first / second step of a block
+  uint32_t sd;            // this lane's scale-or-min dword of the block
+  // k-step j of a k-block: lane quarter kq covers k = 32 kq + 8 j .. +7
+  auto read_x = [&](f16x8& o, int xs, auto j_, int i) __attribute__((always_inline)) {
     constexpr int j = decltype(j_)::value;
+    o = *(const f16x8*)(Xl + xs * XB + (16 * i + r16) * 256 + 16 * ((4 * kq + j) ^ r16));
+  };
+  // Codes: dwords J0, J0 + 1 of the lane's 16 bytes.  Scales: the lane
+  // quarter's 16 k (32 kq + 8 J0 ..) need 8 scale and 8 min dwords; lane d
+  // of the quarter's row of 16 holds scale dword d (d < 8) or min dword d - 8.
+  const int sd_off = (2 * wcol + (r16 >> 3)) * SCH + 64 * kq + 32 * PH + 4 * (r16 & 7);
+  auto read_cs = [&](int wsg) __attribute__((always_inline)) {
+    const uint8_t* cp = Wl + wsg * WBYTES + 4 * wcol * 1024 + lane * 16 + 8 * PH;
     unr<4>([&](auto t_) {
       constexpr int t = decltype(t_)::value;
-      w[t] = dequant8(c[t][j], o.sv, o.mv, dq);
+      const u32x2 v = *(const u32x2*)(cp + t * 1024);
+      c0[t] = v[0];
+      c1[t] = v[1];
     });
+    sd = *(const uint32_t*)(Sl + wsg * SBYTES + sd_off);
   };
-  auto mma = [&](const f16x8 (&w)[4], const f16x8 (&x)[TM]) __attribute__((always_inline)) {
-    unr<TM>([&](auto i_) {
-      constexpr int i = decltype(i_)::value;
-      unr<4>([&](auto t_) {
-        constexpr int t = decltype(t_)::value;
-        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[t], x[i], acc[i][t], 0, 0, 0);
-      });
-    });
-  };
-  // issue order in one k-step: NR LDS reads first, then each MFMA followed by
-  // VPM VALU instructions (the expansion for the next k-step)
-  constexpr int VPM = (56 + 4 * TM - 1) / (4 * TM);
-  auto interleave = [&](auto nr_) __attribute__((always_inline)) {
-    unr<decltype(nr_)::value>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
-    unr<4 * TM>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+  // expansion of the wave's step s (0: first, 1: second) of the block
+  auto expand = [&](const uint32_t (&c)[4], auto s_) __attribute__((always_inline)) {
+    constexpr int s = decltype(s_)::value;
+    const u32x4 sv = {row_bcast<4 * s + 0>(sd), row_bcast<4 * s + 1>(sd), row_bcast<4 * s + 2>(sd),
+                      row_bcast<4 * s + 3>(sd)};
+    const u32x4 mv = {row_bcast<8 + 4 * s + 0>(sd), row_bcast<8 + 4 * s + 1>(sd),
+                      row_bcast<8 + 4 * s + 2>(sd), row_bcast<8 + 4 * s + 3>(sd)};
+    unr<4>([&](auto t_) {
+      constexpr int t = decltype(t_)::value;
+      w[t] = dequant8(c[t], sv, mv, dq);
     });
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
+  using JA = std::integral_constant<int, J0>;      // first step of a block
+  using JB = std::integral_constant<int, J0 + 1>;  // second step
 
-  // One k-block i with codes in `cur`; the codes of block i+1 go to `nxt`.
-  // At entry wa = expanded k-step 0 of block i and sb = its k-step 1 scales.
-  auto block = [&](int i, const u32x4 (&cur)[4], u32x4 (&nxt)[4]) __attribute__((always_inline)) {
-    const int xs = i & 1, wsg = i & 3, wsg1 = (i + 1) & 3;
-    // activations of block i (and codes of block i+1) are in LDS for every
-    // wave; every wave is done with block i-1
-    wait_vm<3, 0>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_x(xa, xs, 0);
-    issue_x(i + 1);
-    issue_ws(i + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    read_x(xb, xs, 1);
-    read_s(sa, wsg, 2);
-    mma(wa, xa);
-    make_w(wb, cur, sb, I1());
-    interleave(std::integral_constant<int, TM + 2>());
-    __builtin_amdgcn_sched_barrier(0);
-    read_x(xa, xs, 2);
-    read_s(sb, wsg, 3);
-    read_c(nxt, wsg1);
-    mma(wb, xb);
-    make_w(wa, cur, sa, I2());
-    interleave(std::integral_constant<int, TM + 6>());
-    __builtin_amdgcn_sched_barrier(0);
-    read_x(xb, xs, 3);
-    read_s(sa, wsg1, 0);
-    mma(wa, xa);
-    make_w(wb, cur, sb, I3());
-    interleave(std::integral_constant<int, TM + 2>());
-    __builtin_amdgcn_sched_barrier(0);
-    read_s(sb, wsg1, 1);
-    mma(wb, xb);
-    make_w(wa, nxt, sa, I0());
-    interleave(std::integral_constant<int, 2>());
+  // One step: MFMAs with the held operands, next step's activations from
+  // buffer xs at k-step jn, and the next step's weights from codes `cn`
+  // (step sn).  `NR` LDS reads (codes and scales of the next block, issued
+  // just before) come first in the issue order.
+  auto step = [&](int xs, auto jn_, const uint32_t (&cn)[4], auto sn_, auto nr_)
+      __attribute__((always_inline)) {
+    constexpr int NR = decltype(nr_)::value;
+    constexpr int T0 = NR == 0 ? 0 : (TM >= 4 ? 2 : (TM >= 2 ? 1 : 0));
+    constexpr int VPM = (60 + 4 * (TM - T0) - 1) / (4 * (TM - T0));
+    const f16x8 wc[4] = {w[0], w[1], w[2], w[3]};
+    unr<TM>([&](auto i_) {
+      constexpr int r = decltype(i_)::value;
+      const f16x8 xr = x[r];
+      unr<4>([&](auto t_) {
+        constexpr int t = decltype(t_)::value;
+        acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc[t], xr, acc[r][t], 0, 0, 0);
+      });
+      read_x(x[r], xs, jn_, r);
+    });
+    expand(cn, sn_);
+    unr<NR>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+    unr<TM>([&](auto i_) {
+      constexpr int r = decltype(i_)::value;
+      unr<4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (r >= T0) __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+      });
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- prologue: codes/scales of blocks 0..2 and activations of block 0
+  // ---- prologue: weights of blocks 0..2, activations of blocks 0 and 1
   issue_ws(0);
-  issue_ws(1);
   issue_x(0);
+  issue_ws(1);
+  issue_x(1);
   issue_ws(2);
-  wait_vm<6 + NX>();  // block 0's codes and scales (own loads)
+  wait_vm<2 * NWS + NX>();  // block 0's loads (own)
   __builtin_amdgcn_s_barrier();
-  read_c(ca, 0);
-  read_s(sa, 0, 0);
-  read_s(sb, 0, 1);
-  make_w(wa, ca, sa, I0());
+  unr<TM>([&](auto i_) { read_x(x[decltype(i_)::value], 0, JA(), decltype(i_)::value); });
+  read_cs(0);
+  expand(c0, I0());
+  __builtin_amdgcn_sched_barrier(0);
 
-  // pairs of blocks, so that the code buffers swap roles without copies
-  int i = 0;
-  for (; i + 2 <= nb; i += 2) {
-    block(i, ca, cb);
-    block(i + 1, cb, ca);
+  for (int i = 0; i < nb; ++i) {
+    // first step of block i; next: the second step (codes already held)
+    step(i & 1, JB(), c1, I1(), I0());
+    // block boundary: this wave's activations of block i are in registers
+    wait_vm<NWS, 0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_x(i + 2);
+    issue_ws(i + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    // second step of block i; next: the first step of block i+1
+    read_cs((i + 1) & 3);
+    step((i + 1) & 1, JA(), c0, I0(), std::integral_constant<int, 5>());
   }
-  if (i < nb) block(i, ca, cb);
-  wait_vm<0>();  // no direct load may still target LDS when the group ends
+  wait_vm<0, 0>();  // every direct load and LDS read of this wave is done
+  __builtin_amdgcn_s_barrier();
 
-  const int n_wave = nt * 256 + wcol * 64;
-  if (n_wave >= g.N) return;
-  // ---- epilogue: lane holds rows 16 (rt0 + i) + r16, columns n .. n+3 ----
+  // ---- add the two halves: the PH = 0 wave finalises row tiles [0, H), the
+  // PH = 1 wave [H, TM); each writes the other's half of its sums to LDS
+  constexpr int H = (TM + 1) / 2;
+  float* xch = (float*)lds + wcol * (TM * 4 * 4 * 64);  // [tile][t][e][lane]
   unr<TM>([&](auto i_) {
     constexpr int i = decltype(i_)::value;
-    const int m = 16 * (rt0 + i) + r16;
-    if (m >= g.M) return;
-    unr<4>([&](auto t_) {
-      constexpr int t = decltype(t_)::value;
-      const int n = n_wave + 16 * t + 4 * kq;
-      f32x4 v = acc[i][t];
-      if (g.P) {
-        *(f32x4*)(g.P + ((int64_t)split * g.M + m) * g.N + n) = v;
-        return;
-      }
-      if (g.relu) {
+    if constexpr ((PH == 0) == (i >= H)) {
+      unr<4>([&](auto t_) {
+        constexpr int t = decltype(t_)::value;
+        *(f32x4*)(xch + ((i * 4 + t) * 64 + lane) * 4) = acc[i][t];
+      });
+    }
+  });
+  wait_vm<0, 0>();  // the exchange writes are done before the barrier
+  __builtin_amdgcn_s_barrier();
+  const int n_wave = nt * 256 + wcol * 64;
+  if (n_wave >= g.N) return;
+  unr<TM>([&](auto i_) {
+    constexpr int i = decltype(i_)::value;
+    if constexpr ((PH == 0) == (i < H)) {
+      const int m = 16 * i + r16;
+      unr<4>([&](auto t_) {
+        constexpr int t = decltype(t_)::value;
+        const int n = n_wave + 16 * t + 4 * kq;
+        f32x4 v = acc[i][t] + *(const f32x4*)(xch + ((i * 4 + t) * 64 + lane) * 4);
+        if (m >= g.M) return;
+        if (g.P) {
+          *(f32x4*)(g.P + ((int64_t)split * g.M + m) * g.N + n) = v;
+          return;
+        }
+        if (g.relu) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
-      }
-      if (g.res) {
-        const f16x4 r = *(const f16x4*)(g.res + m * g.ldr + n);
+          for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
+        }
+        if (g.res) {
+          const f16x4 rr = *(const f16x4*)(g.res + m * g.ldr + n);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += (float)r[e];
-      }
-      f16x4 o;
+          for (int e = 0; e < 4; ++e) v[e] += (float)rr[e];
+        }
+        f16x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (_Float16)v[e];
-      *(f16x4*)(g.Y + m * g.ldy + n) = o;
-    });
+        for (int e = 0; e < 4; ++e) o[e] = (_Float16)v[e];
+        *(f16x4*)(g.Y + m * g.ldy + n) = o;
+      });
+    }
   });
 }
 
-template <int TA, int TB>
+template <int TM>
 __global__ __launch_bounds__(512, 1) void k_gemm_dq(DqArgs g) {
-  constexpr int SR = 32 * ((TA + TB + 1) / 2);
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[XS * SR * 256 + WS * (WBYTES + SBYTES)];
+  constexpr int BYTES = XS * 16 * TM * 256 + WS * (WBYTES + SBYTES);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[BYTES];
+  static_assert(4 * TM * 4 * 4 * 64 * 4 <= BYTES, "the exchange fits in LDS");
   // workgroups on one XCD (id % 8) take a contiguous run of (split, column
   // tile) pairs, split-major, so they share activation k-slices in L2
   const int total = g.ntiles * g.splits;
@@ -292,9 +310,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dq(DqArgs g) {
   const int split = id / g.ntiles, nt = id % g.ntiles;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave < 4)
-    dq_wave<TA, SR>(g, lds, wave, wave, 0, nt, split);
+    dq_pair<TM, 0>(g, lds, wave, nt, split);
   else
-    dq_wave<TB, SR>(g, lds, wave, wave - 4, TA, nt, split);
+    dq_pair<TM, 1>(g, lds, wave, nt, split);
 }
 
 }  // namespace
@@ -324,14 +342,15 @@ hp_status launch_gemm_dq(const void* x, int64_t ldx, const hp_mat& w, int64_t M,
   Prof prof("gemm_q4_skinny", st);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(512), 0, st, a); };
   switch (T) {
-    case 2: go(k_gemm_dq<1, 1>); break;
-    case 3: go(k_gemm_dq<2, 1>); break;
-    case 4: go(k_gemm_dq<2, 2>); break;
-    case 5: go(k_gemm_dq<3, 2>); break;
-    case 6: go(k_gemm_dq<3, 3>); break;
-    case 7: go(k_gemm_dq<4, 3>); break;
-    case 8: go(k_gemm_dq<4, 4>); break;
-    default: go(k_gemm_dq<5, 4>); break;
+    case 1: go(k_gemm_dq<1>); break;
+    case 2: go(k_gemm_dq<2>); break;
+    case 3: go(k_gemm_dq<3>); break;
+    case 4: go(k_gemm_dq<4>); break;
+    case 5: go(k_gemm_dq<5>); break;
+    case 6: go(k_gemm_dq<6>); break;
+    case 7: go(k_gemm_dq<7>); break;
+    case 8: go(k_gemm_dq<8>); break;
+    default: go(k_gemm_dq<9>); break;
   }
   return launch_ok("k_gemm_dq");
 }
