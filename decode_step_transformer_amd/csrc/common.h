@@ -64,10 +64,18 @@ hp_status launch_gemm_dq(const void* x, int64_t ldx, const hp_mat& w, int64_t M,
 
 // fp16 tiled product for tall M (wt = [n][k] fp16) and the int4 -> fp16
 // weight expansion that feeds it.
-hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int k, int n, int64_t M,
-                        const void* res, int64_t ldr, bool relu, void* y, int64_t ldy,
+hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int64_t ldw, int k, int n,
+                        int64_t M, const void* res, int64_t ldr, bool relu, void* y, int64_t ldy,
                         hipStream_t st);
-hp_status launch_expand_q4(const hp_mat& w, void* wt, hipStream_t st);
+// int4 weight -> fp16 wt[n][k] (row stride ldw) for the tall products.
+hp_status launch_expand_q4(const hp_mat& w, void* wt, int64_t ldw, hipStream_t st);
+
+// Row stride (elements of 2 bytes) for an internal [rows][n] fp16 buffer:
+// rows whose byte length is a multiple of 16 KB put the same column of
+// consecutive rows on the same HBM channels, which cut the tall GEMM to
+// three quarters of its speed when such a buffer is its input (measured at
+// n = 49152); 128 bytes more per row break the alias.
+inline int64_t pad_ld(int64_t n) { return n % 8192 == 0 ? n + 64 : n; }
 
 // KV append / attention.  `dpos` (device int32, may be NULL): when set, the
 // kernels read pos from it (plus pos as an offset), so a captured graph can

@@ -334,7 +334,7 @@ static int split_for(int32_t k, int32_t n) {
 
 size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {
   if (M <= 0) return 0;
-  if (M > SKINNY_M) return fmt == HP_Q4 ? (size_t)k * (size_t)n * 2 : 0;  // fp16 expansion
+  if (M > SKINNY_M) return fmt == HP_Q4 ? (size_t)pad_ld(k) * (size_t)n * 2 : 0;  // fp16 expansion
   const int s = fmt == HP_Q4 ? split_rs(k, n) : split_for(k, n);
   return s > 1 ? (size_t)s * (size_t)M * (size_t)n * sizeof(float) : 0;
 }
@@ -396,11 +396,11 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
   // tall products: fp16 MFMA kernel over LDS tiles; int4 weights are first
   // expanded to fp16 into the scratch buffer
   if (q4) {
-    hp_status s = launch_expand_q4(w, ws, st);
+    hp_status s = launch_expand_q4(w, ws, pad_ld(w.k), st);
     if (s != HP_OK) return s;
-    return launch_gemm16(x, ldx, ws, w.k, w.n, M, res, ldr, relu, y, ldy, st);
+    return launch_gemm16(x, ldx, ws, pad_ld(w.k), w.k, w.n, M, res, ldr, relu, y, ldy, st);
   }
-  return launch_gemm16(x, ldx, w.data, w.k, w.n, M, res, ldr, relu, y, ldy, st);
+  return launch_gemm16(x, ldx, w.data, w.k, w.k, w.n, M, res, ldr, relu, y, ldy, st);
 }
 
 }  // namespace hp

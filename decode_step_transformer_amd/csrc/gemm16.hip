@@ -42,7 +42,8 @@ __device__ __forceinline__ void unroll16(F&& f) {
 struct G16Args {
   const _Float16* A;
   int64_t lda, M;
-  const _Float16* W;  // wt[N][K]
+  const _Float16* W;  // wt[N][K], row stride ldw
+  int64_t ldw;
   int K, N, mtiles, ntiles;
   const _Float16* res;
   int64_t ldr;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
     const int64_t m = min(m0 + 16 * (2 * wave + h) + rin, g.M - 1);
     srcA[h] = g.A + m * g.lda + 8 * cchunk;
     const int64_t n = min(n0 + 16 * (2 * wave + h) + rin, g.N - 1);
-    srcB[h] = g.W + n * g.K + 8 * cchunk;
+    srcB[h] = g.W + n * g.ldw + 8 * cchunk;
   }
   const uint32_t sbase = lds_off(S);
   auto issue = [&](int ks, int stage) __attribute__((always_inline)) {
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
 __global__ __launch_bounds__(256) void k_expand_q4(const u32x4* __restrict__ packed,
                                                    const _Float16* __restrict__ scale,
                                                    const _Float16* __restrict__ minv, int K, int N,
-                                                   _Float16* __restrict__ wt) {
+                                                   _Float16* __restrict__ wt, int64_t ldw) {
   const DqConst dq{0x000F000Fu, 0x00F000F0u, in_vgpr(0x64006400u), in_vgpr(0x54005400u)};
   const int KB = K / 128;
   const int64_t total = (int64_t)(N / 16) * KB * 64;
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256) void k_expand_q4(const u32x4* __restrict__ pac
     const u32x4 c = packed[idx];
     const _Float16* sp = scale + (int64_t)(n >> 6) * K + k0;
     const _Float16* mp = minv + (int64_t)(n >> 6) * K + k0;
-    _Float16* out = wt + (int64_t)n * K + k0;
+    _Float16* out = wt + (int64_t)n * ldw + k0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4 s = *(const u32x4*)(sp + 8 * j);
@@ -218,8 +219,8 @@ __global__ __launch_bounds__(256) void k_expand_q4(const u32x4* __restrict__ pac
 
 }  // namespace
 
-hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int k, int n, int64_t M,
-                        const void* res, int64_t ldr, bool relu, void* y, int64_t ldy,
+hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int64_t ldw, int k, int n,
+                        int64_t M, const void* res, int64_t ldr, bool relu, void* y, int64_t ldy,
                         hipStream_t st) {
   if (M == 0) return HP_OK;
   G16Args a;
@@ -227,6 +228,7 @@ hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int k, int n
   a.lda = ldx;
   a.M = M;
   a.W = (const _Float16*)wt;
+  a.ldw = ldw;
   a.K = k;
   a.N = n;
   a.mtiles = (int)cdiv(M, G_BM);
@@ -241,12 +243,12 @@ hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int k, int n
   return launch_ok("k_gemm16");
 }
 
-hp_status launch_expand_q4(const hp_mat& w, void* wt, hipStream_t st) {
+hp_status launch_expand_q4(const hp_mat& w, void* wt, int64_t ldw, hipStream_t st) {
   const int64_t total = (int64_t)(w.n / 16) * (w.k / 128) * 64;
   const int blocks = (int)std::min<int64_t>(cdiv(total, 256), 65536);
   Prof prof("expand_q4", st);
   hipLaunchKernelGGL(k_expand_q4, dim3(blocks), dim3(256), 0, st, (const u32x4*)w.data,
-                     (const _Float16*)w.scale, (const _Float16*)w.minv, w.k, w.n, (_Float16*)wt);
+                     (const _Float16*)w.scale, (const _Float16*)w.minv, w.k, w.n, (_Float16*)wt, ldw);
   return launch_ok("k_expand_q4");
 }
 

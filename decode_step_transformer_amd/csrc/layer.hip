@@ -165,7 +165,7 @@ static Ws ws_layout(const hp_dims& d) {
   w.qkv = o; o += al(M * 3 * d.h1 * 2);
   w.a = o;   o += al(M * d.h1 * 2);
   w.xo = o;  o += al(M * d.h1 * 2);
-  w.hid = o; o += al(M * d.h2 * 2);
+  w.hid = o; o += al(M * pad_ld(d.h2) * 2);
   w.part = o; o += al(part);
   w.xb = o;  o += al(Mp * d.h1 * 2);
   w.t0 = o;  o += al(Md * d.h1 * 2);
@@ -190,8 +190,9 @@ static hp_status layer_tail(const hp_layer& w, int64_t M, int h1, int h2, const 
   _Float16* hid = at<_Float16>(ws, L.hid);
   void* part = at<void>(ws, L.part);
   if ((s = launch_gemm(a, h1, w.wo, M, resid, h1, false, xo, h1, part, st)) != HP_OK) return s;
-  if ((s = launch_gemm(xo, h1, w.w1, M, nullptr, 0, true, hid, h2, part, st)) != HP_OK) return s;
-  return launch_gemm(hid, h2, w.w2, M, xo, h1, false, out, h1, part, st);
+  const int64_t ldh = pad_ld(h2);
+  if ((s = launch_gemm(xo, h1, w.w1, M, nullptr, 0, true, hid, ldh, part, st)) != HP_OK) return s;
+  return launch_gemm(hid, ldh, w.w2, M, xo, h1, false, out, h1, part, st);
 }
 
 static hp_status prefill_body(int b, int s, int h1, int h2, int heads, const hp_layer& w,
