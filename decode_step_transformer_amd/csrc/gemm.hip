@@ -4,11 +4,13 @@
 // to FP16 before the product).
 //
 // Tiling (gfx950, wave64, v_mfma_f32_16x16x32_f16):
-//  * A workgroup is 4 waves and owns a BM x 256 output tile (BM = 16 TM);
-//    wave w owns output columns [64 w, 64 w + 64) = one int4 group, as 4
-//    16-column subtiles, for all BM rows.
+//  * A workgroup is 8 waves and owns a BM x 128 output tile (BM = all M
+//    rows, 16 TM); wave w owns the 16 output columns [16 w, 16 w + 16) for
+//    all BM rows.  The product is bound by streaming the fp16 weights, so
+//    each wave keeps three k-blocks of its weight fragments in flight in
+//    registers (48 VGPRs) and a CU holds up to 16 waves.
 //  * The activation tile x[BM][128] of each k-block is staged through LDS
-//    (double-buffered, rows padded by 16 B) and shared by the 4 waves.
+//    (three stages, rows padded by 16 B) and shared by the 8 waves.
 //  * Weight fragments (fp16, wt[n][k] rows) go straight from HBM to
 //    registers, four 16-byte chunks per lane and subtile per k-block.
 //  * MFMA operand A is the weight fragment (16 output columns), operand B the
@@ -56,11 +58,14 @@ struct GemmArgs {
 
 constexpr int NS = 3;  // LDS activation stages and weight register slots
 
+constexpr int F_WAVES = 8;                 // waves per workgroup
+constexpr int F_COLS = 16 * F_WAVES;       // output columns per workgroup
+
 // Workgroup tile order: workgroups on the same XCD (id % 8) take a contiguous
 // run of tiles, and runs sweep 4 row tiles at a time so that concurrently
 // running tiles share activation and weight k-slices in L2.
 __device__ __forceinline__ void tile_of(const GemmArgs& g, int& mt, int& nt) {
-  const int ntiles = (g.N + 255) / 256;
+  const int ntiles = (g.N + F_COLS - 1) / F_COLS;
   const int total = g.mtiles * ntiles;
   int id = blockIdx.x;
   const int per_xcd = total / 8;
@@ -74,7 +79,7 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, int& mt, int& nt) {
 }
 
 // One wave's part of a workgroup tile: TM 16-row tiles starting at row tile
-// rt0 of the workgroup's rows (from m0), times the 64 output columns of wave
+// rt0 of the workgroup's rows (from m0), times the 16 output columns of wave
 // column wcol.  All NT threads of the workgroup stage SR activation rows per
 // k-block into As (NS stages of SR x LDS_ROW halves).
 template <int TM, int NT, int SR>
@@ -83,11 +88,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int 
   const int lane = tid & 63;
   const int KB = g.K / BK;
   auto As = [&](int stage) __attribute__((always_inline)) { return As_ + stage * (SR * LDS_ROW); };
-  const int n_wave = nt * 256 + wcol * 64;
+  const int n_wave = nt * F_COLS + wcol * 16;
   const bool wave_on = n_wave < g.N;
-  // a wave past the last column reloads the last group (never stored), so
+  // a wave past the last column reloads the last subtile (never stored), so
   // every load is unconditional
-  const int n_ld = min(n_wave, g.N - 64);
+  const int n_ld = min(n_wave, g.N - 16);
   const int split = blockIdx.y;
   const int kb0 = split * KB / g.splits, kb1 = (split + 1) * KB / g.splits;
   auto clampk = [&](int kb) __attribute__((always_inline)) { return min(kb, kb1 - 1); };
@@ -118,27 +123,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int 
   // ---- weight fragments ----
   const int kq = lane >> 4, r16 = lane & 15;
   struct Raw {
-    u32x4 c[16];  // 4 chunks per subtile
+    u32x4 c[4];  // the 4 k-steps of one k-block
   };
   const _Float16* Bh = g.B + (int64_t)(n_ld + r16) * g.K + 32 * kq;
   auto load_b = [&](Raw& R, int kb) __attribute__((always_inline)) {
-    unroll<4>([&](auto t_) {
-      constexpr int t = decltype(t_)::value;
-      const u32x4* p = (const u32x4*)(Bh + (int64_t)16 * t * g.K + (int64_t)kb * BK);
-      unroll<4>([&](auto j_) {
-        constexpr int j = decltype(j_)::value;
-        R.c[4 * t + j] = p[j];
-      });
+    const u32x4* p = (const u32x4*)(Bh + (int64_t)kb * BK);
+    unroll<4>([&](auto j_) {
+      constexpr int j = decltype(j_)::value;
+      R.c[j] = p[j];
     });
   };
 
-  f32x4 acc[TM][4];
-  unroll<TM>([&](auto i_) {
-    unroll<4>([&](auto t_) { acc[decltype(i_)::value][decltype(t_)::value] = f32x4{0.f, 0.f, 0.f, 0.f}; });
-  });
+  f32x4 acc[TM];
+  unroll<TM>([&](auto i_) { acc[decltype(i_)::value] = f32x4{0.f, 0.f, 0.f, 0.f}; });
 
   // ---- one MFMA k-step (32 deep): fragments of (stage, j) ----
-  f16x8 xa[TM], xb[TM], wa[4], wb[4];
+  f16x8 xa[TM], xb[TM], wa, wb;
   auto read_x = [&](f16x8 (&x)[TM], int stage, int j) __attribute__((always_inline)) {
     const _Float16* Ab = As(stage) + (16 * rt0 + r16) * LDS_ROW + 32 * kq + 8 * j;
     unroll<TM>([&](auto i_) {
@@ -146,30 +146,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int 
       x[i] = *(const f16x8*)(Ab + 16 * i * LDS_ROW);
     });
   };
-  auto make_w = [&](f16x8 (&w)[4], const Raw& R, auto j_) __attribute__((always_inline)) {
-    constexpr int j = decltype(j_)::value;
-    unroll<4>([&](auto t_) {
-      constexpr int t = decltype(t_)::value;
-      w[t] = as_f16x8(R.c[4 * t + j]);
-    });
+  auto make_w = [&](f16x8& w, const Raw& R, auto j_) __attribute__((always_inline)) {
+    w = as_f16x8(R.c[decltype(j_)::value]);
   };
-  auto mma = [&](const f16x8 (&w)[4], const f16x8 (&x)[TM]) __attribute__((always_inline)) {
+  auto mma = [&](const f16x8& w, const f16x8 (&x)[TM]) __attribute__((always_inline)) {
     unroll<TM>([&](auto i_) {
       constexpr int i = decltype(i_)::value;
-      unroll<4>([&](auto t_) {
-        constexpr int t = decltype(t_)::value;
-        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[t], x[i], acc[i][t], 0, 0, 0);
-      });
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w, x[i], acc[i], 0, 0, 0);
     });
   };
   // issue order inside one k-step: the LDS reads of the next step first,
-  // then each MFMA followed by two VALU instructions
+  // then the MFMAs
   auto interleave = [&]() __attribute__((always_inline)) {
-    unroll<TM + 2>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
-    unroll<4 * TM>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    });
+    unroll<TM>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+    unroll<TM>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); });
   };
 
   Raw r0, r1, r2;
@@ -233,40 +223,39 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int 
   for (int i = 0; i < TM; ++i) {
     const int64_t m = m0 + 16 * (rt0 + i) + r16;
     if (m >= g.M) continue;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = n_wave + 16 * t + 4 * kq;
-      f32x4 v = acc[i][t];
-      if (g.P) {
-        *(f32x4*)(g.P + ((int64_t)split * g.M + m) * g.N + n) = v;
-        continue;
-      }
-      if (g.relu) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
-      }
-      if (g.res) {
-        const f16x4 r = *(const f16x4*)(g.res + m * g.ldr + n);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += (float)r[e];
-      }
-      f16x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (_Float16)v[e];
-      *(f16x4*)(g.Y + m * g.ldy + n) = o;
+    const int n = n_wave + 4 * kq;
+    f32x4 v = acc[i];
+    if (g.P) {
+      *(f32x4*)(g.P + ((int64_t)split * g.M + m) * g.N + n) = v;
+      continue;
     }
+    if (g.relu) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
+    }
+    if (g.res) {
+      const f16x4 r = *(const f16x4*)(g.res + m * g.ldr + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += (float)r[e];
+    }
+    f16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (_Float16)v[e];
+    *(f16x4*)(g.Y + m * g.ldy + n) = o;
   }
 }
 
-// Products with one row tile per workgroup (or any M): 4 waves, each with all
-// TM row tiles of its 64 columns.
+// Products with one row tile per workgroup (or any M): 8 waves, each with all
+// TM row tiles of its 16 columns; the staged rows are padded to a multiple
+// of 32 so that the 512 threads split them evenly.
 template <int TM>
-__global__ __launch_bounds__(256, (TM <= 4 ? 2 : 1)) void k_gemm(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[NS * 16 * TM * LDS_ROW];
+__global__ __launch_bounds__(512, 2) void k_gemm(GemmArgs g) {
+  constexpr int SR = 32 * ((TM + 1) / 2);
+  __shared__ __attribute__((aligned(16))) _Float16 As[NS * SR * LDS_ROW];
   int mt, nt;
   tile_of(g, mt, nt);
   const int wave = threadIdx.x >> 6;
-  gemm_tile<TM, 256, 16 * TM>(g, As, threadIdx.x, wave, 0, (int64_t)mt * 16 * TM, nt);
+  gemm_tile<TM, 512, SR>(g, As, threadIdx.x, wave, 0, (int64_t)mt * 16 * TM, nt);
 }
 
 // Sums split-k partials in split order, then applies the epilogue.
@@ -319,11 +308,12 @@ static int split_rs(int32_t k, int32_t n) {
   }
   return best;
 }
-// 4-wave kernel: at least 512 workgroups where the k-blocks allow.
+// 8-wave fp16 kernel: at least 256 workgroups where the k-blocks allow (each
+// keeps 96 KB of weight fragments in flight, so one per CU saturates HBM).
 static int split_for(int32_t k, int32_t n) {
   const int KB = k / BK;
-  const int ntiles = (int)cdiv(n, 256);
-  const int want = (int)cdiv(512, ntiles);
+  const int ntiles = (int)cdiv(n, F_COLS);
+  const int want = (int)cdiv(256, ntiles);
   for (int d = 1; d <= KB && d <= 16; ++d)
     if (KB % d == 0 && d >= want) return d;
   int best = 1;
@@ -342,7 +332,7 @@ size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {
 template <int TM>
 static void launch_tm(const GemmArgs& a, dim3 grid, hipStream_t st) {
   Prof prof("gemm_f16_skinny", st);
-  hipLaunchKernelGGL(k_gemm<TM>, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_gemm<TM>, grid, dim3(512), 0, st, a);
 }
 
 hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, const void* res,
@@ -370,7 +360,7 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
       a.splits = splits;
       a.mtiles = 1;
       a.P = splits > 1 ? (float*)ws : nullptr;
-      const dim3 grid((unsigned)cdiv(w.n, 256), splits);
+      const dim3 grid((unsigned)cdiv(w.n, F_COLS), splits);
       switch ((int)cdiv(M, 16)) {
         case 1: launch_tm<1>(a, grid, st); break;
         case 2: launch_tm<2>(a, grid, st); break;
