@@ -157,7 +157,7 @@ template <int D, bool Q4>
 struct DecShape {
   static constexpr int LPR = Q4 ? D / 32 : D / 8;
   static constexpr int RPI = 64 / LPR;
-  static constexpr int U = (Q4 && D == 64) ? 2 : 4;
+  static constexpr int U = Q4 ? 2 : 4;  // int4: 115 VGPRs, 4 waves per SIMD
   static constexpr int CR = U * RPI;             // rows per chunk
   static constexpr int RB = Q4 ? D / 2 : 2 * D;  // bytes per cache row
   static constexpr int NA = Q4 ? 32 : 8;         // value dims per lane
@@ -571,16 +571,22 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_lane = 0.f;
   auto visible = [&](int kidx) __attribute__((always_inline)) { return kidx <= qi && kidx < s; };
+  auto all_visible = [](int) __attribute__((always_inline)) { return true; };
 
-  issue(0, 0);
-  for (int kb = 0; kb < nkb; ++kb) {
+  auto block = [&](int kb, auto vis) __attribute__((always_inline)) {
     const int st = kb & 1;
     wait_vm<0, 0>();
     __builtin_amdgcn_s_barrier();
     if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
     const uint8_t* Kl = lds + st * STAGE;
-    flash_block<D>(Kl, Kl + PF_KB * RB, qf, kb * PF_KB, visible, c2, m_run, l_lane, o);
-  }
+    flash_block<D>(Kl, Kl + PF_KB * RB, qf, kb * PF_KB, vis, c2, m_run, l_lane, o);
+  };
+  // blocks left of the diagonal are visible to every query of the group (no
+  // per-key mask), then the diagonal block
+  issue(0, 0);
+  int kb = 0;
+  for (; kb < nkb - 1; ++kb) block(kb, all_visible);
+  block(kb, visible);
   wait_vm<0>();
   flash_store<D>(qi < s ? a.out + ((int64_t)r * s + qi) * a.h1 + h * D : nullptr, l_lane, o);
 }
@@ -684,6 +690,7 @@ __global__ __launch_bounds__(256) void k_multi_attn(DecArgs a) {
     const bool tree = a.masks ? (bool)((mask >> (t & 63u)) & 1ull) : (int)t <= qi;
     return kidx < R && (kidx < P || tree);
   };
+  auto all_visible = [](int) __attribute__((always_inline)) { return true; };
 
   const int nkb = (R + 63) / 64;
   issue(0, 0);
@@ -709,7 +716,11 @@ __global__ __launch_bounds__(256) void k_multi_attn(DecArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile writes are done
     __builtin_amdgcn_s_barrier();
-    flash_block<D>(tiles, tiles + 64 * RB, qf, kb * 64, visible, c2, m_run, l_lane, o);
+    // prefix-only blocks are visible to every query: no per-key mask there
+    if (kb * 64 + 64 <= P)
+      flash_block<D>(tiles, tiles + 64 * RB, qf, kb * 64, all_visible, c2, m_run, l_lane, o);
+    else
+      flash_block<D>(tiles, tiles + 64 * RB, qf, kb * 64, visible, c2, m_run, l_lane, o);
   }
   wait_vm<0>();
   flash_store<D>(qi < a.q ? a.out + ((int64_t)r * a.q + qi) * a.h1 + h * D : nullptr, l_lane, o);
