@@ -55,9 +55,10 @@ size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt);
 hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, const void* res,
                       int64_t ldr, bool relu, void* y, int64_t ldy, void* ws, hipStream_t st);
 
-// Skinny int4 product (1 <= M <= 144) on the 8-wave decode kernel;
-// with splits > 1 the k-range is split and fp32 partials go to `partials`
-// ([splits][M][n]) for k_splitk_reduce.
+// Skinny int4 product (1 <= M <= 144) on the 8-wave decode kernel; with
+// splits > 1 the k-range is split, fp32 partials go to `partials` (the
+// kernel's tile-major layout, gemm_ws_bytes of them) and a second kernel adds
+// them in split order.
 hp_status launch_gemm_dq(const void* x, int64_t ldx, const hp_mat& w, int64_t M, const void* res,
                          int64_t ldr, bool relu, void* y, int64_t ldy, int splits, float* partials,
                          hipStream_t st);

@@ -325,7 +325,12 @@ static int split_for(int32_t k, int32_t n) {
 size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {
   if (M <= 0) return 0;
   if (M > SKINNY_M) return fmt == HP_Q4 ? (size_t)pad_ld(k) * (size_t)n * 2 : 0;  // fp16 expansion
-  const int s = fmt == HP_Q4 ? split_rs(k, n) : split_for(k, n);
+  if (fmt == HP_Q4) {  // tile-major partials of k_gemm_dq: padded to 256 columns, 16-row tiles
+    const int s = split_rs(k, n);
+    return s > 1 ? (size_t)s * (size_t)cdiv(n, 256) * 256 * (size_t)cdiv(M, 16) * 16 * sizeof(float)
+                 : 0;
+  }
+  const int s = split_for(k, n);
   return s > 1 ? (size_t)s * (size_t)M * (size_t)n * sizeof(float) : 0;
 }
 
@@ -341,41 +346,37 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
   const bool q4 = w.fmt == HP_Q4;
   if (M <= SKINNY_M) {
     const int splits = q4 ? split_rs(w.k, w.n) : split_for(w.k, w.n);
-    if (q4) {
-      hp_status s = launch_gemm_dq(x, ldx, w, M, res, ldr, relu, y, ldy, splits, (float*)ws, st);
-      if (s != HP_OK) return s;
-    } else {
-      GemmArgs a;
-      a.A = (const _Float16*)x;
-      a.lda = ldx;
-      a.M = M;
-      a.B = (const _Float16*)w.data;
-      a.K = w.k;
-      a.N = w.n;
-      a.res = (const _Float16*)res;
-      a.ldr = ldr;
-      a.relu = relu ? 1 : 0;
-      a.Y = (_Float16*)y;
-      a.ldy = ldy;
-      a.splits = splits;
-      a.mtiles = 1;
-      a.P = splits > 1 ? (float*)ws : nullptr;
-      const dim3 grid((unsigned)cdiv(w.n, F_COLS), splits);
-      switch ((int)cdiv(M, 16)) {
-        case 1: launch_tm<1>(a, grid, st); break;
-        case 2: launch_tm<2>(a, grid, st); break;
-        case 3: launch_tm<3>(a, grid, st); break;
-        case 4: launch_tm<4>(a, grid, st); break;
-        case 5: launch_tm<5>(a, grid, st); break;
-        case 6: launch_tm<6>(a, grid, st); break;
-        case 7: launch_tm<7>(a, grid, st); break;
-        case 8: launch_tm<8>(a, grid, st); break;
-        default: launch_tm<9>(a, grid, st); break;
-      }
-      hp_status s = launch_ok("k_gemm");
-      if (s != HP_OK) return s;
+    // int4: the kernel and its split-k reduce (tile-major partials) in gemm_dec.hip
+    if (q4) return launch_gemm_dq(x, ldx, w, M, res, ldr, relu, y, ldy, splits, (float*)ws, st);
+    GemmArgs a;
+    a.A = (const _Float16*)x;
+    a.lda = ldx;
+    a.M = M;
+    a.B = (const _Float16*)w.data;
+    a.K = w.k;
+    a.N = w.n;
+    a.res = (const _Float16*)res;
+    a.ldr = ldr;
+    a.relu = relu ? 1 : 0;
+    a.Y = (_Float16*)y;
+    a.ldy = ldy;
+    a.splits = splits;
+    a.mtiles = 1;
+    a.P = splits > 1 ? (float*)ws : nullptr;
+    const dim3 grid((unsigned)cdiv(w.n, F_COLS), splits);
+    switch ((int)cdiv(M, 16)) {
+      case 1: launch_tm<1>(a, grid, st); break;
+      case 2: launch_tm<2>(a, grid, st); break;
+      case 3: launch_tm<3>(a, grid, st); break;
+      case 4: launch_tm<4>(a, grid, st); break;
+      case 5: launch_tm<5>(a, grid, st); break;
+      case 6: launch_tm<6>(a, grid, st); break;
+      case 7: launch_tm<7>(a, grid, st); break;
+      case 8: launch_tm<8>(a, grid, st); break;
+      default: launch_tm<9>(a, grid, st); break;
     }
-    if (splits == 1) return HP_OK;
+    hp_status s = launch_ok("k_gemm");
+    if (s != HP_OK || splits == 1) return s;
     const int64_t quads = M * (w.n / 4);
     const int blocks = (int)std::min<int64_t>(cdiv(quads, 256), 8192);
     Prof prof("gemm_splitk_reduce", st);

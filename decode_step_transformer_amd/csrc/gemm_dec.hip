@@ -25,8 +25,9 @@
 //    swizzled by row (fragment reads of 16 rows hit distinct banks).
 //  * Codes are expanded in registers with the magic-exponent trick and one
 //    packed FMA with scale and min (a single rounding).
-//  * Split partials go to fp32 scratch, summed in split order by
-//    k_splitk_reduce (so a row's result never depends on M).
+//  * Split partials go to fp32 scratch in the kernel's own tile-major order
+//    (each store instruction writes 1 KB contiguous) and are summed in split
+//    order by k_dq_reduce (so a row's result never depends on M).
 #include <type_traits>
 
 #include "common.h"
@@ -275,7 +276,10 @@ __device__ __forceinline__ void dq_pair(const DqArgs& g, uint8_t* lds, int wave,
         f32x4 v = acc[i][t] + *(const f32x4*)(xch + ((i * 4 + t) * 64 + lane) * 4);
         if (m >= g.M) return;
         if (g.P) {
-          *(f32x4*)(g.P + ((int64_t)split * g.M + m) * g.N + n) = v;
+          // tile-major partials: one store instruction writes 1 KB contiguous
+          const int64_t pi =
+              ((((int64_t)split * g.ntiles + nt) * 4 + wcol) * TM + i) * 4 + t;
+          *(f32x4*)(g.P + (pi * 64 + lane) * 4) = v;
           return;
         }
         if (g.relu) {
@@ -315,6 +319,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dq(DqArgs g) {
     dq_pair<TM, 1>(g, lds, wave, nt, split);
 }
 
+// Sums the split partials of k_gemm_dq in split order and applies the
+// epilogue.  Partial layout: [split][column tile][column group][row tile]
+// [subtile][lane] f32x4, lane l holding row 16 (row tile) + l % 16 and
+// columns 16 (subtile) + 4 (l / 16) .. +3 of its group; one thread per f32x4
+// of a split, so the partial reads are contiguous.
+__global__ __launch_bounds__(256) void k_dq_reduce(const float* __restrict__ P, int splits,
+                                                   int ntiles, int tm, int M, int N,
+                                                   const _Float16* __restrict__ res, int64_t ldr,
+                                                   int relu, _Float16* __restrict__ Y,
+                                                   int64_t ldy) {
+  const int64_t per_split = (int64_t)ntiles * 4 * tm * 4 * 64;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < per_split; q += stride) {
+    const int lane = (int)(q & 63), t = (int)((q >> 6) & 3);
+    int64_t rest = q >> 8;
+    const int i = (int)(rest % tm);
+    rest /= tm;
+    const int wcol = (int)(rest & 3), nt = (int)(rest >> 2);
+    const int m = 16 * i + (lane & 15);
+    const int n = nt * 256 + wcol * 64 + 16 * t + 4 * (lane >> 4);
+    if (m >= M || n >= N) continue;
+    f32x4 v = *(const f32x4*)(P + q * 4);
+    for (int s = 1; s < splits; ++s) v += *(const f32x4*)(P + (s * per_split + q) * 4);
+    if (relu) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
+    }
+    if (res) {
+      const f16x4 r = *(const f16x4*)(res + m * ldr + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += (float)r[e];
+    }
+    f16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (_Float16)v[e];
+    *(f16x4*)(Y + m * ldy + n) = o;
+  }
+}
+
 }  // namespace
 
 hp_status launch_gemm_dq(const void* x, int64_t ldx, const hp_mat& w, int64_t M, const void* res,
@@ -352,7 +395,15 @@ hp_status launch_gemm_dq(const void* x, int64_t ldx, const hp_mat& w, int64_t M,
     case 8: go(k_gemm_dq<8>); break;
     default: go(k_gemm_dq<9>); break;
   }
-  return launch_ok("k_gemm_dq");
+  hp_status s = launch_ok("k_gemm_dq");
+  if (s != HP_OK || splits == 1) return s;
+  const int64_t per_split = (int64_t)a.ntiles * 4 * T * 4 * 64;
+  const int blocks = (int)std::min<int64_t>(cdiv(per_split, 256), 8192);
+  Prof prof_r("gemm_splitk_reduce", st);
+  hipLaunchKernelGGL(k_dq_reduce, dim3(blocks), dim3(256), 0, st, (const float*)partials, splits,
+                     a.ntiles, T, (int)M, w.n, (const _Float16*)res, ldr, a.relu, (_Float16*)y,
+                     ldy);
+  return launch_ok("k_dq_reduce");
 }
 
 }  // namespace hp
