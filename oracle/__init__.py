@@ -59,6 +59,8 @@ def lib():
         L.or_kv_append.argtypes = [_int] * 5 + [_p, _p, _int, _int, _p, _p, _p, _p]
         L.or_tree_masks.restype = _int
         L.or_tree_masks.argtypes = [_p, _int, _p]
+        L.or_tree_prune.restype = _int
+        L.or_tree_prune.argtypes = [_p, _int, _int, _p, _p]
         L.or_run_block.argtypes = [_int] * 9 + [_p, _p, _p, _int, _int, _p, _p, _p, _p, _p, _p]
         _lib = L
     return _lib
@@ -164,6 +166,28 @@ def tree_masks(parent) -> np.ndarray:
     if rc != 0:
         raise ValueError("invalid parent array")
     return m
+
+
+def tree_prune(parent, u: int):
+    """[SpecPipe] sub-tree pruning: (new_parent [nq], src [nq], kept) for verified token u."""
+    p = _c(parent, np.int32)
+    new_parent = np.zeros(p.shape[0], np.int32)
+    src = np.zeros(p.shape[0], np.int32)
+    kept = lib().or_tree_prune(_ptr(p), p.shape[0], int(u), _ptr(new_parent), _ptr(src))
+    if kept < 0:
+        raise ValueError("invalid parent array or verified index")
+    return new_parent, src, kept
+
+
+def kv_compact(kv, pos: int, src, kept):
+    """Moves kept tree rows into place: for request r, rows pos + j (j < kept[r]) of every
+    head take rows pos + src[r][j] (K and V, codes and scale/min); other rows untouched."""
+    for r in range(kv.b):
+        idx = pos + np.asarray(src[r][:kept[r]], np.int64)
+        dst = slice(pos, pos + int(kept[r]))
+        for arr in (kv.k, kv.v, kv.ksm, kv.vsm):
+            if arr is not None:
+                arr[r][:, dst] = arr[r][:, idx].copy()
 
 
 # ----------------------------------------------------------------- layers

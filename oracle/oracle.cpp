@@ -397,6 +397,44 @@ int or_tree_masks(const int32_t* parent, int nq, uint64_t* mask) {
   return 0;
 }
 
+// ------------------------------------------------------------ tree pruning
+// [SpecPipe] 2.2.1 (sub-tree pruning, Fig. 5-b) and 2.2.2 (Fig. 8): once
+// token u is verified, the token arrays keep the subtree rooted at u (the
+// tokens whose column-u entry of M is set: u and its descendants), and the
+// cache keeps the rows of the verified path, u's ancestors, which every kept
+// token sees.  Kept tokens are the ancestors of u and u's subtree, in their
+// BFS order; the parent of a kept token is its old parent's new index.
+// Slots j >= kept get filler leaves (parent of the last kept token, or 0
+// when only one token is kept) so that new_parent stays a valid BFS array.
+// src[j] = old index of kept token j.  Returns the kept count, or -1 when
+// the parent array is invalid or u is outside [0, nq).
+int or_tree_prune(const int32_t* parent, int nq, int u, int32_t* new_parent, int32_t* src) {
+  uint64_t mask[64];
+  if (or_tree_masks(parent, nq, mask) != 0 || u < 0 || u >= nq) return -1;
+  int newidx[64];
+  int kept = 0;
+  for (int i = 0; i < nq; ++i) {
+    const bool ancestor_of_u = (mask[u] >> i) & 1ull;  // i on the path from u to the root
+    const bool in_subtree = (mask[i] >> u) & 1ull;     // u on the path from i to the root
+    newidx[i] = -1;
+    if (ancestor_of_u || in_subtree) {
+      newidx[i] = kept;
+      src[kept] = i;
+      ++kept;
+    }
+  }
+  for (int j = 0; j < kept; ++j) {
+    const int p = parent[src[j]];
+    new_parent[j] = p < 0 ? -1 : newidx[p];
+  }
+  const int fill = kept == 1 ? 0 : new_parent[kept - 1];
+  for (int j = kept; j < nq; ++j) {
+    new_parent[j] = fill;
+    src[j] = -1;
+  }
+  return kept;
+}
+
 // ------------------------------------------------------------ block schedule
 // [FlexGen] section 4 (computation schedule, Algorithm 1 and Fig. 3): a block
 // of b = gbs x (b / gbs) requests; generation step i = 0 is the prefill
