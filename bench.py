@@ -18,7 +18,8 @@ Prints one JSON line (rank 0, N = 1 only):
   decode_kernels-- the same for the decode-phase kernels (one eager decode
                    column after the timed region);
   tree_attention-- the tree-masked decode attention workload (8 requests,
-                   2048-row int4 prefix, 64 tree tokens), event-timed;
+                   2048-row int4 prefix, 64 tree tokens), event-timed, with the
+                   pruning plan and cache compaction after verification;
   cpu_baseline  -- the CPU oracle timed on a bounded sample of the same
                    workload (one decode layer for a few requests).
 """
@@ -142,12 +143,44 @@ def tree_attention(hp, torch, stream, reps=20):
     ms = e0.elapsed_time(e1) / reps
     cache_bytes = 2.0 * b * H * (P + q) * (D / 2 + 4 * D / 64)
     flops = 4.0 * D * b * H * q * P                       # prefix part; tree rows add < 2%
+    prune = tree_prune_step(hp, torch, stream, g, parent.cuda(), kv, reps)
     return {"workload": f"tree-masked decode attention b={b} h1={h1} heads={H} prefix={P} q={q} "
                         "int4 cache",
             "avg_us": ms * 1e3, "bound": "hbm", "gbs": cache_bytes / (ms / 1e3) / 1e9,
             "frac_hbm": cache_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             "tflops": flops / (ms / 1e3) / 1e12,
-            "work": "cache bytes 2*b*heads*(prefix+q)*(d/2 + 4*d/64) per launch, one read"}
+            "work": "cache bytes 2*b*heads*(prefix+q)*(d/2 + 4*d/64) per launch, one read",
+            "prune": prune}
+
+
+def tree_prune_step(hp, torch, stream, g, parent, kv, reps):
+    """After verification ([SpecPipe] 2.2.1 sub-tree pruning, 2.2.2 cache compaction):
+    the pruning plan for one verified token per request, then the move of the kept
+    tree rows of every head's K and V cache; both event-timed over `reps` calls."""
+    t = TREE
+    b, h1, H, P, q = t["b"], t["h1"], t["heads"], t["prefix"], t["q"]
+    D = h1 // H
+    verified = torch.randint(0, q, (b,), generator=g, device="cuda", dtype=torch.int32)
+    new_parent, src, kept, err = hp.hp_tree_prune(parent, verified, stream=stream)
+    hp.hp_kv_compact(b, q, h1, H, P, src, kept, kv, stream=stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        hp.hp_tree_prune(parent, verified, stream=stream)
+    ev[1].record(stream)
+    for _ in range(reps):  # the same plan each time: the same rows move
+        hp.hp_kv_compact(b, q, h1, H, P, src, kept, kv, stream=stream)
+    ev[2].record(stream)
+    stream.synchronize()
+    assert int(err.item()) == 0
+    plan_ms = ev[0].elapsed_time(ev[1]) / reps
+    move_ms = ev[1].elapsed_time(ev[2]) / reps
+    ks = kept.cpu().tolist()
+    moved = 2.0 * H * sum(ks) * (D / 2 + 4 * D / 64) * 2  # each kept K/V row read and written
+    return {"plan_us": plan_ms * 1e3, "compact_us": move_ms * 1e3, "kept": ks,
+            "compact_gbs": moved / (move_ms / 1e3) / 1e9,
+            "work": "kept rows x heads x (K, V) x (d/2 + 4*d/64) bytes, read and written once; "
+                    "launch-bound at this size"}
 
 
 def cpu_baseline(c, cname, seconds_hint=20.0):

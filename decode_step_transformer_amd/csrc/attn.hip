@@ -764,6 +764,128 @@ __global__ __launch_bounds__(64) void k_tree_masks(int b, int q, const int32_t* 
   }
 }
 
+// ------------------------------------------------------------ tree pruning
+// [SpecPipe] 2.2.1 sub-tree pruning (Fig. 5-b) and 2.2.2 (Fig. 8): once
+// token u of a request is verified, the request keeps the tokens on u's path
+// to the root (the verified path, whose cache rows every kept token sees) and
+// u's subtree (the tokens with u as an ancestor), in BFS order.  One wave
+// walks every request; lane i holds token i: its ancestor mask as in
+// k_tree_masks, a ballot of the kept lanes gives each kept token its new
+// index, and a lane shuffle maps its parent to the parent's new index.
+// Slots past the kept count become filler leaves (the last kept token's
+// parent, or 0 when one token is kept) so the new array stays a valid BFS
+// parent array.  A request with an invalid parent array or verified index
+// keeps nothing and is counted in err.
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__global__ __launch_bounds__(64) void k_tree_prune(int b, int q, const int32_t* __restrict__ parent,
+                                                   const int32_t* __restrict__ verified,
+                                                   int32_t* __restrict__ new_parent,
+                                                   int32_t* __restrict__ src,
+                                                   int32_t* __restrict__ kept_out,
+                                                   int32_t* __restrict__ err) {
+  const int i = threadIdx.x;
+  int nbad = 0;
+  for (int r = 0; r < b; ++r) {
+    const int32_t* pr = parent + (int64_t)r * q;
+    int p0 = -1;
+    bool ok = true;
+    uint64_t m = 0;
+    if (i < q) {
+      p0 = pr[i];
+      ok = (i == 0) ? (p0 == -1) : (p0 >= 0 && p0 < i);
+      m = 1ull << i;
+      if (ok) {
+        int t = p0;
+        while (t >= 0) {  // valid parents strictly decrease: the walk ends
+          m |= 1ull << t;
+          const int pt = pr[t];
+          if (!(t == 0 ? pt == -1 : (pt >= 0 && pt < t))) {
+            ok = false;
+            break;
+          }
+          t = pt;
+        }
+      }
+    }
+    const int u = verified[r];
+    const bool good = !__any(!ok) && u >= 0 && u < q;
+    int32_t* npr = new_parent + (int64_t)r * q;
+    int32_t* sr = src + (int64_t)r * q;
+    if (!good) {
+      if (i == 0) {
+        kept_out[r] = 0;
+        ++nbad;
+      }
+      if (i < q) {
+        npr[i] = i == 0 ? -1 : 0;
+        sr[i] = -1;
+      }
+      continue;
+    }
+    const uint64_t mu = shfl_u64(m, u);
+    const bool keep = i < q && (((mu >> i) & 1ull) || ((m >> u) & 1ull));
+    const uint64_t kb = __ballot(keep);
+    const int newidx = __popcll(kb & ((1ull << i) - 1ull));  // kept lanes below i
+    const int kept = __popcll(kb);
+    const int nidx_of_parent = __shfl(newidx, p0 < 0 ? 0 : p0);
+    const int np = p0 < 0 ? -1 : nidx_of_parent;
+    const int last = 63 - __clzll(kb);  // lane of the last kept token
+    const int np_last = __shfl(np, last);
+    const int fill = kept == 1 ? 0 : np_last;
+    if (keep) {
+      npr[newidx] = np;
+      sr[newidx] = i;
+    }
+    if (i < q && i >= kept) {
+      npr[i] = fill;
+      sr[i] = -1;
+    }
+    if (i == 0) kept_out[r] = kept;
+  }
+  if (i == 0 && err) *err = nbad;
+}
+
+// Moves kept tree rows into place after k_tree_prune: one wave per
+// (request, head, K or V); lane j copies the row of kept token j from cache
+// row pos + src[j] to row pos + j (RB bytes of codes or fp16, SMB bytes of
+// scale/min pairs).  Every lane's store depends on its own load and each
+// load instruction covers the whole wave, so all rows are read before any is
+// overwritten.
+template <int RB, int SMB>
+__global__ __launch_bounds__(64) void k_kv_compact(int q, int heads, int pos, int cap,
+                                                   const int32_t* __restrict__ src,
+                                                   const int32_t* __restrict__ kept, uint8_t* k,
+                                                   uint8_t* v, uint8_t* ksm, uint8_t* vsm) {
+  const int j = threadIdx.x;
+  const int t = blockIdx.x & 1, rh = blockIdx.x >> 1;
+  const int h = rh % heads, r = rh / heads;
+  const int n = min(max(kept[r], 0), q);  // any kept / src values stay inside rows [pos, pos + q)
+  const int64_t row0 = (int64_t)(r * heads + h) * cap + pos;
+  uint8_t* base = (t ? v : k) + row0 * RB;
+  uint8_t* sbase = SMB ? (t ? vsm : ksm) + row0 * SMB : nullptr;
+  const int s = j < n ? src[(int64_t)r * q + j] : j;
+  const bool act = j < n && s >= 0 && s < q;
+  u32x4 buf[RB / 16];
+  uint32_t sm[SMB / 4 > 0 ? SMB / 4 : 1];
+  if (act) {
+#pragma unroll
+    for (int c = 0; c < RB / 16; ++c) buf[c] = *(const u32x4*)(base + (int64_t)s * RB + 16 * c);
+#pragma unroll
+    for (int c = 0; c < SMB / 4; ++c) sm[c] = *(const uint32_t*)(sbase + (int64_t)s * SMB + 4 * c);
+  }
+  if (act && s != j) {
+#pragma unroll
+    for (int c = 0; c < RB / 16; ++c) *(u32x4*)(base + (int64_t)j * RB + 16 * c) = buf[c];
+#pragma unroll
+    for (int c = 0; c < SMB / 4; ++c) *(uint32_t*)(sbase + (int64_t)j * SMB + 4 * c) = sm[c];
+  }
+}
+
 // -------------------------------------------------------------- launchers
 void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
                       int32_t pos, const int32_t* dpos, const hp_kv& kv, hipStream_t st) {
@@ -825,6 +947,35 @@ void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* ma
                        hipStream_t st) {
   Prof prof("tree_masks", st);
   hipLaunchKernelGGL(k_tree_masks, dim3(1), dim3(64), 0, st, b, q, parent, masks, err);
+}
+
+void launch_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
+                       int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
+                       hipStream_t st) {
+  Prof prof("tree_prune", st);
+  hipLaunchKernelGGL(k_tree_prune, dim3(1), dim3(64), 0, st, b, q, parent, verified, new_parent,
+                     src, kept, err);
+}
+
+void launch_kv_compact(int32_t b, int32_t q, int32_t heads, int32_t d, int32_t pos,
+                       const int32_t* src, const int32_t* kept, const hp_kv& kv, hipStream_t st) {
+  const dim3 grid((unsigned)(2 * b * heads));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, q, heads, pos, kv.cap, src, kept,
+                       (uint8_t*)kv.k, (uint8_t*)kv.v, (uint8_t*)kv.k_sm, (uint8_t*)kv.v_sm);
+  };
+  Prof prof("kv_compact", st);
+  if (kv.fmt == HP_Q4) {
+    if (d == 128)
+      go(k_kv_compact<64, 8>);
+    else
+      go(k_kv_compact<32, 4>);
+  } else {
+    if (d == 128)
+      go(k_kv_compact<256, 0>);
+    else
+      go(k_kv_compact<128, 0>);
+  }
 }
 
 }  // namespace hp

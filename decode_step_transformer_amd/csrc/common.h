@@ -90,6 +90,11 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
                              const hp_kv& kv, void* out, hipStream_t st);
 void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
                        hipStream_t st);
+void launch_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
+                       int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
+                       hipStream_t st);
+void launch_kv_compact(int32_t b, int32_t q, int32_t heads, int32_t d, int32_t pos,
+                       const int32_t* src, const int32_t* kept, const hp_kv& kv, hipStream_t st);
 
 // Small utility kernels used by the block runner.
 void launch_copy_step(const void* src, int64_t count_elems, int64_t stride_elems,

@@ -425,6 +425,33 @@ hp_status hp_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* m
   return launch_ok("k_tree_masks");
 }
 
+hp_status hp_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
+                        int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
+                        void* stream) {
+  if (b <= 0) return fail(HP_ERR_SHAPE, "b must be positive");
+  if (q < 1 || q > 64) return fail(HP_ERR_TREE, "q must be in [1, 64]");
+  if (!parent || !verified || !new_parent || !src || !kept) return fail(HP_ERR_NULL, "NULL pointer");
+  hp_status s = device_check();
+  if (s != HP_OK) return s;
+  launch_tree_prune(b, q, parent, verified, new_parent, src, kept, err, S(stream));
+  return launch_ok("k_tree_prune");
+}
+
+hp_status hp_kv_compact(int32_t b, int32_t q, int32_t h1, int32_t heads, int32_t pos,
+                        const int32_t* src, const int32_t* kept, const hp_kv* kv, void* stream) {
+  if (b <= 0 || h1 <= 0 || heads <= 0 || h1 % heads || pos < 0)
+    return fail(HP_ERR_SHAPE, "bad sizes");
+  if (q < 1 || q > 64) return fail(HP_ERR_TREE, "q must be in [1, 64]");
+  const int D = h1 / heads;
+  if (D != 64 && D != 128) return fail(HP_ERR_SHAPE, "head dim %d not in {64, 128}", D);
+  if (!src || !kept) return fail(HP_ERR_NULL, "NULL pointer");
+  hp_status s = check_kv(kv, pos + q);
+  if (s != HP_OK) return s;
+  if ((s = device_check()) != HP_OK) return s;
+  launch_kv_compact(b, q, heads, D, pos, src, kept, *kv, S(stream));
+  return launch_ok("k_kv_compact");
+}
+
 size_t hp_workspace_bytes(const hp_dims* d) {
   if (check_dims(d) != HP_OK) return 0;
   return ws_layout(*d).total;

@@ -48,6 +48,7 @@ EXPORTS = [
     "hp_last_error", "hp_device_check", "hp_quantize_g64", "hp_dequantize_g64",
     "hp_pack_weight_q4", "hp_pack_weight_f16", "hp_gemm_workspace_bytes", "hp_gemm",
     "hp_kv_append", "hp_prefill_attention", "hp_decode_attention", "hp_tree_masks",
+    "hp_tree_prune", "hp_kv_compact",
     "hp_workspace_bytes", "hp_layer_prefill", "hp_layer_decode", "hp_run_block",
     "hp_release_graphs", "hp_weight_bytes", "hp_kv_bytes", "hp_profile", "hp_profile_read",
 ]
@@ -75,6 +76,8 @@ def lib():
             "hp_prefill_attention": [_i32, _i32, _i32, _i32, _p, _p, _p],
             "hp_decode_attention": [_i32, _i32, _i32, _i32, _p, _i32, _p, C.POINTER(hp_kv), _p, _p],
             "hp_tree_masks": [_i32, _i32, _p, _p, _p, _p],
+            "hp_tree_prune": [_i32, _i32, _p, _p, _p, _p, _p, _p, _p],
+            "hp_kv_compact": [_i32, _i32, _i32, _i32, _i32, _p, _p, C.POINTER(hp_kv), _p],
             "hp_layer_prefill": [C.POINTER(hp_dims), C.POINTER(hp_layer), _p, C.POINTER(hp_kv), _p,
                                  _p, _sz, _p],
             "hp_layer_decode": [C.POINTER(hp_dims), C.POINTER(hp_layer), _p, _i32, _i32, _p,
@@ -262,6 +265,24 @@ def hp_tree_masks(parent: torch.Tensor, stream=None):
     err = torch.empty(1, dtype=torch.int32, device=parent.device)
     _check(lib().hp_tree_masks(b, q, _ptr(parent), _ptr(masks), _ptr(err), _stream(stream)))
     return masks, err
+
+
+def hp_tree_prune(parent: torch.Tensor, verified: torch.Tensor, stream=None):
+    """parent int32 [b][q], verified int32 [b] (device) -> (new_parent, src, kept, err)."""
+    b, q = parent.shape
+    new_parent = torch.empty((b, q), dtype=torch.int32, device=parent.device)
+    src = torch.empty((b, q), dtype=torch.int32, device=parent.device)
+    kept = torch.empty(b, dtype=torch.int32, device=parent.device)
+    err = torch.empty(1, dtype=torch.int32, device=parent.device)
+    _check(lib().hp_tree_prune(b, q, _ptr(parent), _ptr(verified), _ptr(new_parent), _ptr(src),
+                               _ptr(kept), _ptr(err), _stream(stream)))
+    return new_parent, src, kept, err
+
+
+def hp_kv_compact(b, q, h1, heads, pos, src, kept, kv: KVCache, stream=None):
+    c = kv.c()
+    _check(lib().hp_kv_compact(b, q, h1, heads, pos, _ptr(src), _ptr(kept), C.byref(c),
+                               _stream(stream)))
 
 
 # ------------------------------------------------------------------ layers

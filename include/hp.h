@@ -198,6 +198,32 @@ hp_status hp_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, c
 hp_status hp_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks,
                         int32_t* err, void* stream);
 
+/* [SpecPipe] 2.2.1 sub-tree pruning (Fig. 5-b) and 2.2.2 (Fig. 8): when
+ * token verified[r] of request r's BFS tree of q tokens is verified, the
+ * request keeps the tokens on its path to the root (the verified path,
+ * whose cache rows every kept token sees) and its subtree, in BFS order.
+ * parent: device int32 [b][q] (rules of hp_tree_masks); verified: device
+ * int32 [b].  Outputs (device int32): kept[r] = number of kept tokens;
+ * src[r][j] = old index of kept token j (j < kept[r], else -1);
+ * new_parent[r][j] = new index of its parent (-1 for the root); entries
+ * j >= kept[r] are filler leaves (the last kept token's parent, or 0 when
+ * one token is kept), so new_parent is again a valid BFS parent array.  A
+ * request with an invalid parent array or verified index outside [0, q)
+ * keeps nothing (kept 0, new_parent a star, src -1); err (device int32, or
+ * NULL) is set to the number of such requests.  q in [1, 64]; one
+ * single-wave kernel launch. */
+hp_status hp_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
+                        int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
+                        void* stream);
+
+/* Moves one layer's kept tree rows into place after hp_tree_prune: for
+ * request r and every head, cache row pos + j (j < kept[r]) takes the K and
+ * V rows (codes and scale/min, or fp16) of row pos + src[r][j].  Rows
+ * [0, pos) and [pos + kept[r], pos + q) are not touched.  src, kept: device
+ * int32 as written by hp_tree_prune.  Requires pos + q <= kv->cap. */
+hp_status hp_kv_compact(int32_t b, int32_t q, int32_t h1, int32_t heads, int32_t pos,
+                        const int32_t* src, const int32_t* kept, const hp_kv* kv, void* stream);
+
 /* ------------------------------------------------------------- layers */
 /* Workspace for hp_layer_prefill / hp_layer_decode / hp_run_block with these
  * dims (bytes of device memory, 256-byte aligned by the caller). */

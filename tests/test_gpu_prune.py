@@ -1,0 +1,119 @@
+"""GPU token-tree pruning and KV compaction against the oracle (SpecPipe
+article, 2.2.1 sub-tree pruning, Fig. 5-b; 2.2.2, Fig. 8).
+
+Plans (kept count, old indices, new parents) and compacted cache rows must be
+bit-exact; attention of the kept tokens over the compacted cache is then
+checked against the oracle within the parity tolerance.
+"""
+import numpy as np
+import pytest
+
+import synth
+from helpers import TOL, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+SEED = synth.seed_for(70)
+
+
+@pytest.fixture(scope="module")
+def hp():
+    import torch
+    from decode_step_transformer_amd import hp as _hp
+    assert torch.cuda.is_available()
+    assert _hp.hp_device_check() == 0, _hp.hp_last_error()
+    return _hp
+
+
+def _trees(b, q, stream0):
+    return np.stack([synth.bfs_parents(SEED, stream0 + r, q) for r in range(b)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("q", [1, 5, 64])
+def test_tree_prune_matches_oracle(hp, orc, q):
+    b = 8
+    parent = _trees(b, q, 100 + q)
+    verified = (synth.words(SEED, 200 + q, 0, b) % np.uint64(q)).astype(np.int32)
+    new_parent, src, kept, err = hp.hp_tree_prune(dev(parent), dev(verified))
+    new_parent, src, kept = host(new_parent), host(src), host(kept)
+    assert int(host(err)[0]) == 0
+    for r in range(b):
+        rp, rs, rk = orc.tree_prune(parent[r], int(verified[r]))
+        assert int(kept[r]) == rk
+        assert np.array_equal(new_parent[r], rp) and np.array_equal(src[r], rs)
+
+
+def test_tree_prune_rejects_bad_requests(hp, orc):
+    q = 8
+    parent = _trees(3, q, 300)
+    parent[1, 5] = 6                       # parent after its child
+    verified = np.array([2, 3, q], np.int32)  # request 2: index out of range
+    new_parent, src, kept, err = hp.hp_tree_prune(dev(parent), dev(verified))
+    kept, new_parent = host(kept), host(new_parent)
+    assert int(host(err)[0]) == 2
+    assert list(kept) == [orc.tree_prune(parent[0], 2)[2], 0, 0]
+    for r in (1, 2):  # a request that keeps nothing gets a valid star
+        orc.tree_masks(new_parent[r])
+
+
+@pytest.mark.parametrize("fmt,heads,h1", [(1, 2, 256), (1, 4, 256), (0, 2, 256), (0, 2, 128)])
+def test_kv_compact_matches_oracle(hp, orc, fmt, heads, h1):
+    b, pos, q = 3, 37, 64
+    D = h1 // heads
+    cap = pos + q + 3
+    kv = hp.KVCache(fmt, b, heads, cap, D)
+    rk = orc.KV(fmt, b, heads, cap, D)
+    qkv = synth.normal_f16(SEED, 400 + fmt, (b, pos + q, 3 * h1))
+    hp.hp_kv_append(b, pos + q, h1, heads, dev(qkv), 0, kv)
+    for which in ("k", "v"):
+        setattr(rk, which, host(getattr(kv, which)).copy())
+    if fmt == 1:
+        rk.ksm, rk.vsm = host(kv.k_sm).copy(), host(kv.v_sm).copy()
+    parent = _trees(b, q, 500)
+    verified = np.array([0, 9, 63], np.int32)
+    new_parent, src, kept, err = hp.hp_tree_prune(dev(parent), dev(verified))
+    hp.hp_kv_compact(b, q, h1, heads, pos, src, kept, kv)
+    orc.kv_compact(rk, pos, host(src), host(kept))
+    pairs = [("k", "k"), ("v", "v")] + ([("k_sm", "ksm"), ("v_sm", "vsm")] if fmt == 1 else [])
+    for name, oname in pairs:  # bit patterns, fp16 rows included
+        g, r = host(getattr(kv, name)), getattr(rk, oname)
+        assert np.array_equal(g.view(np.uint8), r.view(np.uint8)), name
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_attention_after_pruning(hp, orc, fmt):
+    """Kept tokens attend over the compacted cache with the new masks: the
+    result matches the oracle's attention of those tokens before pruning."""
+    b, heads, h1, pos, q = 4, 4, 512, 300, 64
+    D = h1 // heads
+    kv = hp.KVCache(fmt, b, heads, pos + q, D)
+    pre = synth.normal_f16(SEED, 600 + fmt, (b, pos, 3 * h1))
+    qkv = synth.normal_f16(SEED, 610 + fmt, (b, q, 3 * h1))
+    hp.hp_kv_append(b, pos, h1, heads, dev(pre), 0, kv)
+    hp.hp_kv_append(b, q, h1, heads, dev(qkv), pos, kv)
+    parent = _trees(b, q, 700)
+    masks, _ = hp.hp_tree_masks(dev(parent))
+    before = host(hp.hp_decode_attention(b, q, h1, heads, dev(qkv), pos, kv, masks=masks))
+    verified = np.array([0, 3, 20, 63], np.int32)
+    new_parent, src, kept, err = hp.hp_tree_prune(dev(parent), dev(verified))
+    hp.hp_kv_compact(b, q, h1, heads, pos, src, kept, kv)
+    new_masks, e2 = hp.hp_tree_masks(new_parent)
+    assert int(host(e2)[0]) == 0
+    srch, kepth = host(src), host(kept)
+    qkv2 = np.zeros_like(qkv)
+    for r in range(b):  # queries of the kept tokens, in their new slots
+        qkv2[r, :kepth[r]] = qkv[r, srch[r, :kepth[r]]]
+    after = host(hp.hp_decode_attention(b, q, h1, heads, dev(qkv2), pos, kv, masks=new_masks))
+    ok = orc.KV(fmt, b, heads, pos + q, D)
+    for name, oname in (("k", "k"), ("v", "v")) + ((("k_sm", "ksm"), ("v_sm", "vsm")) if fmt else ()):
+        setattr(ok, oname, host(getattr(kv, name)).copy())
+    Kc, Vc = ok.values("k", pos + q), ok.values("v", pos + q)
+    nm = orc.tree_masks
+    for r in range(b):
+        k = int(kepth[r])
+        m = nm(host(new_parent)[r])[:k]
+        for h in range(heads):
+            ref = orc.attention(qkv2[r, :k, h * D:(h + 1) * D], Kc[r, h], Vc[r, h],
+                                np.full(k, pos, np.int32), m, pos)
+            assert_close(after[r, :k, h * D:(h + 1) * D], ref, what=f"r{r} h{h}")
+        # the same tokens before pruning, within the tolerance (block boundaries moved)
+        assert_close(after[r, :k], before[r, srch[r, :k]], tol=TOL, what=f"r{r} before/after")
