@@ -159,6 +159,30 @@ def attention(q, k, v, lim, mask=None, tbase=0) -> np.ndarray:
     return out.view(np.float16)
 
 
+def topk_count(T: int) -> int:
+    """[FlexGen] section 5 (sparse attention): the top 10% of the T cached tokens,
+    read as ceil(T / 10), at least one."""
+    return max(1, -(-int(T) // 10))
+
+
+def topk_attention(q, k, v, topk: int):
+    """[FlexGen] section 5, sparse attention: one query q[d] against the cached keys
+    k[T][d] and values v[T][d] (binary16 values, dequantised where the cache is int4).
+    Scores z_j = q . k_j (double; the 1/sqrt(d) scale does not change the order); the
+    topk largest are kept, ties going to the lower index; the other tokens are dropped
+    and the output is the attention over the kept keys alone (the softmax renormalised
+    over them).  Returns (out binary16 [d], kept indices in ascending order)."""
+    qb, kb, vb = _bits(q).reshape(-1), _bits(k), _bits(v)
+    T = kb.shape[0]
+    if not 1 <= topk <= T:
+        raise ValueError("topk must be in [1, T]")
+    z = h2f(kb).astype(np.float64) @ h2f(qb).astype(np.float64)
+    order = np.argsort(-z, kind="stable")  # descending; equal scores keep index order
+    kept = np.sort(order[:topk])
+    out = attention(qb.reshape(1, -1), kb[kept], vb[kept], [topk])[0]
+    return out, kept
+
+
 def tree_masks(parent) -> np.ndarray:
     p = _c(parent, np.int32)
     m = np.zeros(p.shape[0], np.uint64)
