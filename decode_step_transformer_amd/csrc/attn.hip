@@ -727,40 +727,61 @@ __global__ __launch_bounds__(256) void k_multi_attn(DecArgs a) {
 }
 
 // ------------------------------------------------------------ tree masks
-// [SpecPipe] 2.2.1: token i sees itself and its ancestors.  One workgroup
-// walks every request; an entry breaking the parent rules keeps only its own
-// bit and is counted.
-__global__ __launch_bounds__(64) void k_tree_masks(int b, int q, const int32_t* __restrict__ parent,
-                                                   uint64_t* __restrict__ masks,
-                                                   int32_t* __restrict__ err) {
-  __shared__ int bad[64];
-  const int i = threadIdx.x;
-  int nbad = 0;
-  for (int r = 0; r < b; ++r) {
-    if (i < q) {
-      const int32_t* pr = parent + (int64_t)r * q;
-      const int p0 = pr[i];
-      const bool ok = (i == 0) ? (p0 == -1) : (p0 >= 0 && p0 < i);
-      nbad += ok ? 0 : 1;
-      uint64_t m = 1ull << i;
-      if (ok) {
-        int u = p0;
-        while (u >= 0) {  // parents strictly decrease along valid links
-          m |= 1ull << u;
-          const int pu = pr[u];
-          if (!(u == 0 ? pu == -1 : (pu >= 0 && pu < u))) break;
-          u = pu;
-        }
-      }
-      masks[(int64_t)r * q + i] = m;
+// [SpecPipe] 2.2.1: token i sees itself and its ancestors.  Lane i of a
+// wave holds token i of one request.  The ancestor sets come from pointer
+// jumping over lane shuffles: after round k, m holds the tokens at distance
+// 0 .. 2^k - 1 above token i and a the one at distance 2^k (-1 past the
+// root); six rounds cover any depth below 64.  A token whose own parent
+// entry breaks the rules (ok false) is treated as a root, so a valid token's
+// set stops at, and includes, the first such ancestor.
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t ancestor_set(int i, int q, int p0, bool ok) {
+  uint64_t m = i < q ? 1ull << i : 0ull;
+  int a = (i < q && ok) ? p0 : -1;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const int from = a < 0 ? i : a;  // every lane takes part in the shuffles
+    const uint64_t ma = shfl_u64(m, from);
+    const int aa = __shfl(a, from);
+    if (a >= 0) {
+      m |= ma;
+      a = aa;
     }
   }
-  bad[i] = nbad;
+  return m;
+}
+
+__device__ __forceinline__ bool parent_ok(int i, int p) {
+  return i == 0 ? p == -1 : (p >= 0 && p < i);
+}
+
+// One wave per request (up to 16 waves, each taking every 16th request); an
+// entry breaking the parent rules keeps only its own bit and is counted.
+__global__ __launch_bounds__(1024) void k_tree_masks(int b, int q, const int32_t* __restrict__ parent,
+                                                     uint64_t* __restrict__ masks,
+                                                     int32_t* __restrict__ err) {
+  __shared__ int bad[16];
+  const int i = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int nbad = 0;
+  for (int r = w; r < b; r += nw) {
+    const int p0 = i < q ? parent[(int64_t)r * q + i] : -1;
+    const bool ok = i >= q || parent_ok(i, p0);
+    nbad += ok ? 0 : 1;
+    const uint64_t m = ancestor_set(i, q, p0, ok);
+    if (i < q) masks[(int64_t)r * q + i] = m;
+  }
+  for (int o = 32; o > 0; o >>= 1) nbad += __shfl_xor(nbad, o);
+  if (i == 0) bad[w] = nbad;
   __syncthreads();
-  if (i == 0) {
+  if (threadIdx.x == 0 && err) {
     int t = 0;
-    for (int j = 0; j < 64; ++j) t += bad[j];
-    if (err) *err = t;
+    for (int j = 0; j < nw; ++j) t += bad[j];
+    *err = t;
   }
 }
 
@@ -768,50 +789,26 @@ __global__ __launch_bounds__(64) void k_tree_masks(int b, int q, const int32_t* 
 // [SpecPipe] 2.2.1 sub-tree pruning (Fig. 5-b) and 2.2.2 (Fig. 8): once
 // token u of a request is verified, the request keeps the tokens on u's path
 // to the root (the verified path, whose cache rows every kept token sees) and
-// u's subtree (the tokens with u as an ancestor), in BFS order.  One wave
-// walks every request; lane i holds token i: its ancestor mask as in
-// k_tree_masks, a ballot of the kept lanes gives each kept token its new
-// index, and a lane shuffle maps its parent to the parent's new index.
-// Slots past the kept count become filler leaves (the last kept token's
-// parent, or 0 when one token is kept) so the new array stays a valid BFS
-// parent array.  A request with an invalid parent array or verified index
-// keeps nothing and is counted in err.
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
-  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__global__ __launch_bounds__(64) void k_tree_prune(int b, int q, const int32_t* __restrict__ parent,
-                                                   const int32_t* __restrict__ verified,
-                                                   int32_t* __restrict__ new_parent,
-                                                   int32_t* __restrict__ src,
-                                                   int32_t* __restrict__ kept_out,
-                                                   int32_t* __restrict__ err) {
-  const int i = threadIdx.x;
+// u's subtree (the tokens with u as an ancestor), in BFS order.  One wave per
+// request; lane i holds token i: its ancestor set as in k_tree_masks, a
+// ballot of the kept lanes gives each kept token its new index, and a lane
+// shuffle maps its parent to the parent's new index.  Slots past the kept
+// count become filler leaves (the last kept token's parent, or 0 when one
+// token is kept) so the new array stays a valid BFS parent array.  A request
+// with an invalid parent array or verified index keeps nothing and is
+// counted in err.
+__global__ __launch_bounds__(1024) void k_tree_prune(int b, int q, const int32_t* __restrict__ parent,
+                                                     const int32_t* __restrict__ verified,
+                                                     int32_t* __restrict__ new_parent,
+                                                     int32_t* __restrict__ src,
+                                                     int32_t* __restrict__ kept_out,
+                                                     int32_t* __restrict__ err) {
+  __shared__ int bad[16];
+  const int i = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int nbad = 0;
-  for (int r = 0; r < b; ++r) {
-    const int32_t* pr = parent + (int64_t)r * q;
-    int p0 = -1;
-    bool ok = true;
-    uint64_t m = 0;
-    if (i < q) {
-      p0 = pr[i];
-      ok = (i == 0) ? (p0 == -1) : (p0 >= 0 && p0 < i);
-      m = 1ull << i;
-      if (ok) {
-        int t = p0;
-        while (t >= 0) {  // valid parents strictly decrease: the walk ends
-          m |= 1ull << t;
-          const int pt = pr[t];
-          if (!(t == 0 ? pt == -1 : (pt >= 0 && pt < t))) {
-            ok = false;
-            break;
-          }
-          t = pt;
-        }
-      }
-    }
+  for (int r = w; r < b; r += nw) {
+    const int p0 = i < q ? parent[(int64_t)r * q + i] : -1;
+    const bool ok = i >= q || parent_ok(i, p0);
     const int u = verified[r];
     const bool good = !__any(!ok) && u >= 0 && u < q;
     int32_t* npr = new_parent + (int64_t)r * q;
@@ -827,6 +824,7 @@ __global__ __launch_bounds__(64) void k_tree_prune(int b, int q, const int32_t* 
       }
       continue;
     }
+    const uint64_t m = ancestor_set(i, q, p0, true);
     const uint64_t mu = shfl_u64(m, u);
     const bool keep = i < q && (((mu >> i) & 1ull) || ((m >> u) & 1ull));
     const uint64_t kb = __ballot(keep);
@@ -847,7 +845,13 @@ __global__ __launch_bounds__(64) void k_tree_prune(int b, int q, const int32_t* 
     }
     if (i == 0) kept_out[r] = kept;
   }
-  if (i == 0 && err) *err = nbad;
+  if (i == 0) bad[w] = nbad;
+  __syncthreads();
+  if (threadIdx.x == 0 && err) {
+    int t = 0;
+    for (int j = 0; j < nw; ++j) t += bad[j];
+    *err = t;
+  }
 }
 
 // Moves kept tree rows into place after k_tree_prune: one wave per
@@ -946,15 +950,16 @@ void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, c
 void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
                        hipStream_t st) {
   Prof prof("tree_masks", st);
-  hipLaunchKernelGGL(k_tree_masks, dim3(1), dim3(64), 0, st, b, q, parent, masks, err);
+  hipLaunchKernelGGL(k_tree_masks, dim3(1), dim3(64 * std::min(b, 16)), 0, st, b, q, parent,
+                     masks, err);
 }
 
 void launch_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
                        int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
                        hipStream_t st) {
   Prof prof("tree_prune", st);
-  hipLaunchKernelGGL(k_tree_prune, dim3(1), dim3(64), 0, st, b, q, parent, verified, new_parent,
-                     src, kept, err);
+  hipLaunchKernelGGL(k_tree_prune, dim3(1), dim3(64 * std::min(b, 16)), 0, st, b, q, parent,
+                     verified, new_parent, src, kept, err);
 }
 
 void launch_kv_compact(int32_t b, int32_t q, int32_t heads, int32_t d, int32_t pos,

@@ -382,18 +382,20 @@ hp_status launch_gemm_dq(const void* x, int64_t ldx, const hp_mat& w, int64_t M,
   a.P = splits > 1 ? partials : nullptr;
   const dim3 grid((unsigned)(a.ntiles * splits));
   const int T = (int)cdiv(M, 16);
-  Prof prof("gemm_q4_skinny", st);
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(512), 0, st, a); };
-  switch (T) {
-    case 1: go(k_gemm_dq<1>); break;
-    case 2: go(k_gemm_dq<2>); break;
-    case 3: go(k_gemm_dq<3>); break;
-    case 4: go(k_gemm_dq<4>); break;
-    case 5: go(k_gemm_dq<5>); break;
-    case 6: go(k_gemm_dq<6>); break;
-    case 7: go(k_gemm_dq<7>); break;
-    case 8: go(k_gemm_dq<8>); break;
-    default: go(k_gemm_dq<9>); break;
+  {
+    Prof prof("gemm_q4_skinny", st);  // the product alone; the reduce is timed on its own
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(512), 0, st, a); };
+    switch (T) {
+      case 1: go(k_gemm_dq<1>); break;
+      case 2: go(k_gemm_dq<2>); break;
+      case 3: go(k_gemm_dq<3>); break;
+      case 4: go(k_gemm_dq<4>); break;
+      case 5: go(k_gemm_dq<5>); break;
+      case 6: go(k_gemm_dq<6>); break;
+      case 7: go(k_gemm_dq<7>); break;
+      case 8: go(k_gemm_dq<8>); break;
+      default: go(k_gemm_dq<9>); break;
+    }
   }
   hp_status s = launch_ok("k_gemm_dq");
   if (s != HP_OK || splits == 1) return s;

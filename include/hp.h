@@ -211,7 +211,7 @@ hp_status hp_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* m
  * request with an invalid parent array or verified index outside [0, q)
  * keeps nothing (kept 0, new_parent a star, src -1); err (device int32, or
  * NULL) is set to the number of such requests.  q in [1, 64]; one
- * single-wave kernel launch. */
+ * kernel launch (one wave per request). */
 hp_status hp_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
                         int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
                         void* stream);

@@ -28,9 +28,8 @@ def _trees(b, q, stream0):
     return np.stack([synth.bfs_parents(SEED, stream0 + r, q) for r in range(b)]).astype(np.int32)
 
 
-@pytest.mark.parametrize("q", [1, 5, 64])
-def test_tree_prune_matches_oracle(hp, orc, q):
-    b = 8
+@pytest.mark.parametrize("b,q", [(8, 1), (8, 5), (8, 64), (37, 64), (16, 33)])
+def test_tree_prune_matches_oracle(hp, orc, b, q):
     parent = _trees(b, q, 100 + q)
     verified = (synth.words(SEED, 200 + q, 0, b) % np.uint64(q)).astype(np.int32)
     new_parent, src, kept, err = hp.hp_tree_prune(dev(parent), dev(verified))
@@ -40,6 +39,32 @@ def test_tree_prune_matches_oracle(hp, orc, q):
         rp, rs, rk = orc.tree_prune(parent[r], int(verified[r]))
         assert int(kept[r]) == rk
         assert np.array_equal(new_parent[r], rp) and np.array_equal(src[r], rs)
+
+
+def test_tree_masks_many_requests(hp, orc):
+    """More requests than waves in the launch; one request with a broken
+    entry: its descendants' sets stop at (and include) that entry, the
+    entry itself keeps only its own bit (hp_tree_masks contract)."""
+    b, q = 37, 64
+    parent = _trees(b, q, 800)
+    ref = np.stack([orc.tree_masks(p) for p in parent])
+    masks, err = hp.hp_tree_masks(dev(parent))
+    assert int(host(err)[0]) == 0
+    assert np.array_equal(host(masks).view(np.uint64), ref)
+    bad = parent.copy()
+    bad[20, 10] = 40
+    masks, err = hp.hp_tree_masks(dev(bad))
+    assert int(host(err)[0]) == 1
+    got = host(masks).view(np.uint64)
+    assert np.array_equal(np.delete(got, 20, 0), np.delete(ref, 20, 0))
+    for i in range(q):  # walk up from i, stopping after the broken entry
+        want, t = 0, i
+        while True:
+            want |= 1 << t
+            if t == 10 or bad[20, t] < 0:
+                break
+            t = int(bad[20, t])
+        assert int(got[20, i]) == want, i
 
 
 def test_tree_prune_rejects_bad_requests(hp, orc):
