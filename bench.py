@@ -16,7 +16,14 @@ Prints one JSON line (rank 0, N = 1 only):
                    events on its own stream through hp_profile, against the
                    published MI355X peak for its bound;
   decode_kernels-- the same for the decode-phase kernels (one eager decode
-                   column after the timed region);
+                   column after the timed region, each launch between its own
+                   event pair);
+  decode_gemm   -- the decode-phase products over all layers' weights,
+                   replayed from a HIP graph (no per-launch event overhead);
+  sparse_attention -- Top-K sparse decode attention (10% of the rows) against
+                   dense decode attention at the decode shape;
+  topk10_block  -- one more block with Top-K sparse attention in its decode
+                   columns (decode tokens/s), unless --no-topk-block;
   tree_attention-- the tree-masked decode attention workload (8 requests,
                    2048-row int4 prefix, 64 tree tokens), event-timed, with the
                    pruning plan and cache compaction after verification;
@@ -105,6 +112,105 @@ def setup(c, seed, hp, torch):
 TREE = dict(b=8, h1=8192, heads=64, prefix=2048, q=64)  # tree-masked decode attention workload
 
 
+def hold_stream(torch, stream, cycles=200_000_000):
+    """Enqueues a bounded spin kernel on `stream` (tens of ms) so that the host can
+    queue a run of short launches before the GPU reaches them; returns an event
+    recorded after the spin (still pending at the end of queueing = queued ahead)."""
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(cycles)
+    ev = torch.cuda.Event()
+    ev.record(stream)
+    return ev
+
+
+def graph_ms(torch, stream, fn, reps=3):
+    """Captures fn's launches on `stream` into one HIP graph and returns the mean
+    event time of a replay (the block itself replays its decode column from a
+    graph; eager stream launches add several microseconds per kernel)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    g.replay()
+    stream.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    stream.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def decode_products(hp, torch, stream, c, layers):
+    """The four decode-phase products of a layer at M = b ([FlexGen] background
+    section: x·w_QKV, ·w_O + residual, relu(·w_1), ·w_2 + residual), each run once per
+    layer (different weights every launch, so nothing is served from a cache),
+    replayed from a HIP graph as the block does; split-K sums included."""
+    b, h1, h2, l = c["b"], c["h1"], c["h2"], c["l"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    x = torch.randn((b, h1), generator=g, device="cuda").half()
+    hid = torch.randn((b, h2), generator=g, device="cuda").half()
+    prods = [("qkv", "wqkv", x, None, False, 3 * h1), ("out", "wo", x, x, False, h1),
+             ("mlp1", "w1", x, None, True, h2), ("mlp2", "w2", hid, x, False, h1)]
+    need = max(hp.hp_gemm_workspace_bytes(b, getattr(layers[0], a).k, n, c["fmt"])
+               for _, a, _, _, _, n in prods)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    outs = {name: torch.empty((b, n), dtype=torch.float16, device="cuda")
+            for name, _, _, _, _, n in prods}
+    per = {}
+    for name, attr, inp, res, relu, _ in prods:
+        def run(attr=attr, inp=inp, res=res, relu=relu, name=name):
+            for j in range(l):
+                hp.hp_gemm(inp, getattr(layers[j], attr), res=res, relu=relu, out=outs[name],
+                           ws=ws, stream=stream)
+        per[name] = graph_ms(torch, stream, run) / l * 1e3
+    layer_us = sum(per.values())
+    tflops = layer_flops(c, b) / (layer_us / 1e6) / 1e12
+    gbs = weight_bytes_per_layer(c) / (layer_us / 1e6) / 1e9
+    return {"avg_us": per, "layer_us": layer_us, "bound": "mfma" if c["fmt"] == 1 else "hbm",
+            "tflops": tflops, "frac_mfma": tflops / MFMA_F16_PEAK_TFLOPS,
+            "gbs_weights": gbs, "frac_hbm_weights": gbs / HBM_PEAK_GBS,
+            "work": "2*b*(4*h1^2 + 2*h1*h2) flops per layer on its weights, M = b; each product "
+                    "over all l layers' weights in turn"}
+
+
+def sparse_attention(hp, torch, stream, c, kvs, cname):
+    """Top-K sparse decode attention ([FlexGen] section 5: keep ceil(T/10) rows per
+    (request, head), read only their V rows) against dense decode attention at the
+    decode shape (one query per request at T = s + n/2 rows), each over every layer's
+    cache in turn, replayed from a HIP graph."""
+    b, h1, H, l = c["b"], c["h1"], c["heads"], c["l"]
+    D = h1 // H
+    T = c["s"] + c["n"] // 2
+    K = -(-T // 10)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    qkv = torch.randn((b, 3 * h1), generator=g, device="cuda").half()
+    out = torch.empty((b, h1), dtype=torch.float16, device="cuda")
+    def run_topk():
+        for kv in kvs:
+            hp.hp_topk_attention(b, h1, H, qkv, T - 1, kv, out=out, stream=stream)
+
+    def run_dense():
+        for kv in kvs:
+            hp.hp_decode_attention(b, 1, h1, H, qkv, T - 1, kv, out=out, stream=stream)
+
+    topk_us = graph_ms(torch, stream, run_topk) / l * 1e3
+    dense_us = graph_ms(torch, stream, run_dense) / l * 1e3
+    row = D * (0.5 + 4 / 64) if c["fmt"] == 1 else 2.0 * D   # cache bytes per row per head
+    topk_bytes = b * H * (T + K) * row                       # every K row, the kept V rows
+    dense_bytes = b * H * 2 * T * row
+    from decode_step_transformer_amd import traffic as tr
+    return {"T": T, "K": K, "topk_us": topk_us, "dense_us": dense_us,
+            "topk_traffic": tr.lookup("k_topk_attn", cname),
+            "topk_gbs": topk_bytes / (topk_us / 1e6) / 1e9,
+            "topk_frac_hbm": topk_bytes / (topk_us / 1e6) / 1e9 / HBM_PEAK_GBS,
+            "dense_gbs": dense_bytes / (dense_us / 1e6) / 1e9, "bound": "hbm",
+            "work": "b*heads*(T + K)*row bytes per Top-K launch (all K rows, K kept V rows), "
+                    "b*heads*2*T*row dense; row = d/2 + 4*d/64 (int4) or 2*d"}
+
+
 def tree_attention(hp, torch, stream, reps=20):
     """The tree-masked decode attention workload ([SpecPipe] 2.2.1 masks over an int4
     cache): b requests, an int4 prefix of `prefix` rows, q tree tokens with random
@@ -164,6 +270,7 @@ def tree_prune_step(hp, torch, stream, g, parent, kv, reps):
     new_parent, src, kept, err = hp.hp_tree_prune(parent, verified, stream=stream)
     hp.hp_kv_compact(b, q, h1, H, P, src, kept, kv, stream=stream)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    held = hold_stream(torch, stream)
     ev[0].record(stream)
     for _ in range(reps):
         hp.hp_tree_prune(parent, verified, stream=stream)
@@ -171,6 +278,7 @@ def tree_prune_step(hp, torch, stream, g, parent, kv, reps):
     for _ in range(reps):  # the same plan each time: the same rows move
         hp.hp_kv_compact(b, q, h1, H, P, src, kept, kv, stream=stream)
     ev[2].record(stream)
+    queued_ahead = not held.query()
     stream.synchronize()
     assert int(err.item()) == 0
     plan_ms = ev[0].elapsed_time(ev[1]) / reps
@@ -178,6 +286,7 @@ def tree_prune_step(hp, torch, stream, g, parent, kv, reps):
     ks = kept.cpu().tolist()
     moved = 2.0 * H * sum(ks) * (D / 2 + 4 * D / 64) * 2  # each kept K/V row read and written
     return {"plan_us": plan_ms * 1e3, "compact_us": move_ms * 1e3, "kept": ks,
+            "queued_ahead": queued_ahead,
             "compact_gbs": moved / (move_ms / 1e3) / 1e9,
             "work": "kept rows x heads x (K, V) x (d/2 + 4*d/64) bytes, read and written once; "
                     "launch-bound at this size"}
@@ -234,6 +343,8 @@ def main():
     ap.add_argument("--config", default="opt-30b-int4", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tree", action="store_true", help="skip the tree-attention workload")
+    ap.add_argument("--no-topk-block", action="store_true",
+                    help="skip the extra block with Top-K sparse decode attention")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; each GPU would run its own block "
@@ -274,21 +385,38 @@ def main():
         wall = time.perf_counter() - t0
         hp.hp_profile(False)
         prof = hp.hp_profile_read()
+        nonfinite = int((~torch.isfinite(t_out.float())).sum().item())
 
         # decode-phase kernels: one eager decode column (cache rows already
-        # filled by the timed blocks), each launch timed with HIP events
+        # filled by the timed blocks), each launch timed with HIP events; the
+        # column is queued behind a spin kernel so that no event pair spans
+        # a wait for the host's next launch
         T = c["s"] + c["n"] // 2
-        hp.hp_profile(True)
         tcur = t_in[0].contiguous()
         tnext = torch.empty_like(tcur)
+        held = hold_stream(torch, stream)
+        hp.hp_profile(True)
         for j in range(c["l"]):
             hp.hp_layer_decode(d, layers[j], tcur, T - 1, 1, kvs[j], tnext, ws, stream=stream)
             tcur, tnext = tnext, tcur
+        dec_queued_ahead = not held.query()
         stream.synchronize()
         hp.hp_profile(False)
         dprof = hp.hp_profile_read()
+        dgemm = decode_products(hp, torch, stream, c, layers)
+        sparse = sparse_attention(hp, torch, stream, c, kvs, args.config)
+        topk_block = None
+        if not args.no_topk_block and c["s"] + c["n"] <= 4096:
+            # the same block with 10% Top-K attention in every decode column
+            tk = hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws,
+                                 hp.HP_GRAPH | hp.HP_TOPK10, timing=True, stream=stream)
+            tk = hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws,
+                                 hp.HP_GRAPH | hp.HP_TOPK10, timing=True, stream=stream)
+            topk_block = {"decode_ms": tk[1], "prefill_ms": tk[0],
+                          "tokens_per_s": c["b"] * c["n"] / (tk[1] / 1e3),
+                          "work": "one block as timed above (second run, graph cached) with "
+                                  "HP_TOPK10: ceil(T/10) rows per (request, head) in decode"}
         tree = None if args.no_tree else tree_attention(hp, torch, stream)
-    nonfinite = int((~torch.isfinite(t_out.float())).sum().item())
 
     b, n, s, l = c["b"], c["n"], c["s"], c["l"]
     K = args.steps
@@ -361,6 +489,10 @@ def main():
         "nonfinite_decode_outputs": nonfinite,
         "roofline": roof,
         "decode_kernels": dec,
+        "decode_kernels_queued_ahead": dec_queued_ahead,
+        "decode_gemm": dgemm,
+        "sparse_attention": sparse,
+        "topk10_block": topk_block,
         "tree_attention": tree,
         "kernels": {k: {"launches": v[0], "total_ms": v[1]} for k, v in prof.items()},
     }

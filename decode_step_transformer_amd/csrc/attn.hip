@@ -5,25 +5,16 @@
 //
 // Decode attention is HBM-bound (about 1 flop per byte of packed cache), so
 // it runs on the vector ALUs, one wave per (request, head, query), streaming
-// the cache in chunks:
-//  * each lane reads 16 consecutive bytes of a row (4 lanes per int4 row of
-//    128 dims), so one load instruction covers whole rows; the loads are
-//    non-temporal and the next chunk's K (V) is requested as soon as the
-//    current chunk's scores (values) are formed;
-//  * codes become halves off + c with a shift and one and-or; in the score
-//    every code reads 64 + c and the offsets cancel against the
-//    accumulator's start value -64 sum(q); the group scale and min are
-//    factored out: s = sum_g scale_g (q . c)_g + min_g (sum q)_g;
-//  * online softmax over chunks with DPP reductions;
-//  * values: sum_t p_t v_t = sum_t (p_t scale_t) c_t + sum_t p_t min_t, the
-//    first term with one mixed-precision FMA per code (binary16 off + c,
-//    fp32 weight and sum), the offsets removed once at the end with the sum
-//    of the weights.
-// Prefill attention reads the fresh fp16 K/V of the prompt (causal) on MFMA;
-// see the section below.
+// the cache in chunks with the row slices, scores and value sums of
+// decode_dev.h; the loads are non-temporal and the next chunk's K (V) is
+// requested as soon as the current chunk's scores (values) are formed; the
+// softmax is online over chunks with DPP reductions.
+// Multi-query decode (tree tokens) and prefill attention run on MFMA; see
+// their sections below.
 #include <math.h>
 
 #include "common.h"
+#include "decode_dev.h"
 #include "dequant_dev.h"
 #include "lds_dma.h"
 #include "quant_dev.h"
@@ -76,20 +67,6 @@ __global__ __launch_bounds__(256) void k_kv_append(AppendArgs a) {
   }
 }
 
-// ------------------------------------------------------------ reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-__device__ __forceinline__ f16x2 h2_of(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
-
 // ------------------------------------------------------- decode attention
 struct DecArgs {
   const _Float16* qkv;
@@ -103,79 +80,13 @@ struct DecArgs {
   const uint32_t* vsm;
   _Float16* out;
 };
-
-// Cross-lane moves on the DPP path (no LDS round trip).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int DPP_HALF_MIRROR = 0x141;
-constexpr int DPP_MIRROR = 0x140;
-constexpr int DPP_ROR = 0x120;        // + 1..15: rotate right within a row of 16 lanes
-
-// sum over aligned groups of N lanes (N = 1, 2, 4, 8, 16): every lane gets its group's sum
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (N >= 2) v += dpp<DPP_XOR1>(v);
-  if constexpr (N >= 4) v += dpp<DPP_XOR2>(v);
-  if constexpr (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
-  if constexpr (N >= 16) v += dpp<DPP_MIRROR>(v);
-  return v;
-}
-// sum over the lanes congruent modulo N (N = 1, 2, 4, 8, 16): every lane gets the total
-template <int N>
-__device__ __forceinline__ float strided_sum(float v) {
-  if constexpr (N <= 1) v += dpp<DPP_ROR + 1>(v);
-  if constexpr (N <= 2) v += dpp<DPP_ROR + 2>(v);
-  if constexpr (N <= 4) v += dpp<DPP_ROR + 4>(v);
-  if constexpr (N <= 8) v += dpp<DPP_ROR + 8>(v);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
-// wave-uniform maximum: DPP within each row of 16 lanes, then the four rows
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp<DPP_XOR1>(v));
-  v = fmaxf(v, dpp<DPP_XOR2>(v));
-  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
-  v = fmaxf(v, dpp<DPP_MIRROR>(v));
-  const int b = __builtin_bit_cast(int, v);
-  return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
-                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
-               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
-                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
-}
-
-// Lane geometry of the streaming decode kernel.  Every lane reads 16
-// consecutive bytes of one cache row; LPR lanes cover a row, one load
-// instruction covers RPI consecutive rows and a chunk is U such loads for K
-// and for V (the next chunk is loaded while the current one is computed).
-template <int D, bool Q4>
-struct DecShape {
-  static constexpr int LPR = Q4 ? D / 32 : D / 8;
-  static constexpr int RPI = 64 / LPR;
-  static constexpr int U = Q4 ? 2 : 4;  // int4: 115 VGPRs, 4 waves per SIMD
-  static constexpr int CR = U * RPI;             // rows per chunk
-  static constexpr int RB = Q4 ? D / 2 : 2 * D;  // bytes per cache row
-  static constexpr int NA = Q4 ? 32 : 8;         // value dims per lane
-};
-
-// one chunk's share of this lane: 16 code bytes per row and (Q4) the row's
-// scale/min pair of this lane's group, for K or for V
-template <int U, bool Q4>
-struct DecPart {
-  u32x4 c[U];
-  uint32_t sm[Q4 ? U : 1];
-};
-
 template <int D, bool Q4, bool MASKED>
 __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   using S = DecShape<D, Q4>;
-  constexpr int LPR = S::LPR, RPI = S::RPI, U = S::U, CR = S::CR, RB = S::RB, NA = S::NA;
-  constexpr int G = D / 64;
+  constexpr int LPR = S::LPR, RPI = S::RPI, RB = S::RB, G = S::G;
+  // a chunk is U loads of RPI rows for K and for V; the next chunk is loaded
+  // while the current one is computed (int4: 118 VGPRs, 4 waves per SIMD)
+  constexpr int U = Q4 ? 2 : 4, CR = U * RPI;
   const int lane = threadIdx.x;
   const int qd = lane % LPR, rho = lane / LPR;
   const int i = blockIdx.x % a.q;
@@ -196,39 +107,9 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   const float c2 = 1.44269504088896341f / sqrtf((float)D);
 
   const DqConst dq{0x000F000Fu, 0x00F000F0u, in_vgpr(0x64006400u), in_vgpr(0x54005400u)};
-
-  // This lane's slice of the query, paired in the order the codes expand
-  // (Q4: pair p of dword j = dims (8j+p, 8j+p+4)).  In the score an expanded
-  // code reads 64 + c (every nibble is moved to bits 4..7 of a half under the
-  // exponent of 64); the accumulator starts at -64 sum(q), so it ends at
-  // sum(c * q).  The small offset keeps the cancelled magnitude, and so the
-  // fp32 rounding of the running sum, near that of sum(c * q) itself.
-  constexpr int NQ = Q4 ? 16 : 4;
-  f16x2 q2[NQ];
-  float corr = 0.f, qsum = 0.f;
-  {
-    const _Float16* qp = a.qkv + ((int64_t)r * a.q + i) * 3 * a.h1 + h * D + (Q4 ? 32 : 8) * qd;
-#pragma unroll
-    for (int j = 0; j < NQ / 4; ++j) {
-      const f16x8 qh = *(const f16x8*)(qp + 8 * j);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        if constexpr (Q4) {
-          q2[4 * j + p] = f16x2{qh[p], qh[p + 4]};
-          corr += 64.f * ((float)qh[p] + (float)qh[p + 4]);
-          qsum += (float)qh[p] + (float)qh[p + 4];
-        } else {
-          q2[4 * j + p] = f16x2{qh[2 * p], qh[2 * p + 1]};
-        }
-      }
-    }
-    if constexpr (Q4) qsum = group_sum<LPR / G>(qsum);  // sum of q over this lane's group
-  }
-
-  float acc[NA];
-#pragma unroll
-  for (int e = 0; e < NA; ++e) acc[e] = 0.f;
-  float bsum = 0.f, pm = 0.f;  // Q4: sum of the weights p*scale, sum of p*min (this group)
+  DecQuery<D, Q4> Q;
+  Q.load(a.qkv + ((int64_t)r * a.q + i) * 3 * a.h1 + h * D + (Q4 ? 32 : 8) * qd);
+  DecAcc<D, Q4> A;
   float m_run = -INFINITY, l_lane = 0.f;
 
   // rows past the visible range are clamped to its last row (their weight is 0)
@@ -255,32 +136,10 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   load(K, kb, ksb, 0);
   load(V, vb, vsb, 0);
   for (int c = 0; c < nc; ++c) {
-    // scores
     float s[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float t;
-      if constexpr (Q4) {
-        t = -corr;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // every pair at bits 4..7 / 20..23 under the exponent of 64
-          const uint32_t w = K.c[u][j];
-          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w << 4, dq.magic1)), q2[4 * j + 0], t, false);
-          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w, dq.magic1)), q2[4 * j + 1], t, false);
-          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w >> 4, dq.magic1)), q2[4 * j + 2], t, false);
-          t = __builtin_amdgcn_fdot2(h2_of(bfi(dq.mask1, w >> 8, dq.magic1)), q2[4 * j + 3], t, false);
-        }
-        t = group_sum<LPR / G>(t);  // sum(c * q) over the group
-        const f16x2 sm = h2_of(K.sm[u]);
-        t = fmaf((float)sm[0], t, (float)sm[1] * qsum);
-        if constexpr (G == 2) t += dpp<DPP_XOR2>(t);
-      } else {
-        t = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) t = __builtin_amdgcn_fdot2(h2_of(K.c[u][j]), q2[j], t, false);
-        t = group_sum<LPR>(t);
-      }
+      const float t = row_score<D, Q4>(K.c[u], Q4 ? K.sm[u] : 0u, Q, dq);
       const int row = c * CR + rho + RPI * u;
       bool valid = row < R;
       if constexpr (MASKED)
@@ -305,78 +164,11 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
       ps += p[u];
     }
     l_lane = fmaf(l_lane, alpha, ps);
-    if (alpha != 1.f) {
-#pragma unroll
-      for (int e = 0; e < NA; ++e) acc[e] *= alpha;
-      bsum *= alpha;
-      pm *= alpha;
-    }
-    // values
-    if constexpr (Q4) {
-      // weights p * scale stay in fp32: each code meets its row's weight in
-      // one mixed-precision FMA (binary16 code, fp32 weight and sum)
-      float bw[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const f16x2 sm = h2_of(V.sm[u]);
-        bw[u] = p[u] * (float)sm[0];
-        bsum += bw[u];
-        pm = fmaf(p[u], (float)sm[1], pm);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t x = V.c[u][j], x8 = x >> 8;
-          const f16x2 c04 = h2_of(bfi(dq.mask0, x, dq.magic0));   // codes 8j, 8j+4 (+1024)
-          const f16x2 c15 = h2_of(bfi(dq.mask1, x, dq.magic1));   // codes 8j+1, 8j+5 (+64)
-          const f16x2 c26 = h2_of(bfi(dq.mask0, x8, dq.magic0));  // codes 8j+2, 8j+6 (+1024)
-          const f16x2 c37 = h2_of(bfi(dq.mask1, x8, dq.magic1));  // codes 8j+3, 8j+7 (+64)
-          float* A = acc + 8 * j;
-          A[0] = fmaf((float)c04[0], bw[u], A[0]);
-          A[4] = fmaf((float)c04[1], bw[u], A[4]);
-          A[1] = fmaf((float)c15[0], bw[u], A[1]);
-          A[5] = fmaf((float)c15[1], bw[u], A[5]);
-          A[2] = fmaf((float)c26[0], bw[u], A[2]);
-          A[6] = fmaf((float)c26[1], bw[u], A[6]);
-          A[3] = fmaf((float)c37[0], bw[u], A[3]);
-          A[7] = fmaf((float)c37[1], bw[u], A[7]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const f16x8 vh = __builtin_bit_cast(f16x8, V.c[u]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf((float)vh[e], p[u], acc[e]);
-      }
-    }
+    if (alpha != 1.f) A.rescale(alpha);
+    A.add(V, p, dq);
     load(V, vb, vsb, c + 1);
   }
-
-  // combine the row slots; every row's weight was counted by its LPR lanes
-  const float l = strided_sum<1>(l_lane) * (1.0f / LPR);
-#pragma unroll
-  for (int e = 0; e < NA; ++e) acc[e] = strided_sum<LPR>(acc[e]);
-  if constexpr (Q4) {
-    bsum = strided_sum<LPR>(bsum);
-    pm = strided_sum<LPR>(pm);
-  }
-  if (rho == 0) {
-    const float inv = 1.0f / l;
-    _Float16* o = a.out + ((int64_t)r * a.q + i) * a.h1 + h * D + (Q4 ? 32 : 8) * qd;
-#pragma unroll
-    for (int j = 0; j < NA / 8; ++j) {
-      f16x8 y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[8 * j + e];
-        if constexpr (Q4) v = v - ((e & 1) ? 64.f : 1024.f) * bsum + pm;
-        y[e] = (_Float16)(v * inv);
-      }
-      *(f16x8*)(o + 8 * j) = y;
-    }
-  }
+  A.finish(l_lane, rho, a.out + ((int64_t)r * a.q + i) * a.h1 + h * D + (Q4 ? 32 : 8) * qd);
 }
 
 // ------------------------------------------------------ prefill attention
@@ -726,170 +518,6 @@ __global__ __launch_bounds__(256) void k_multi_attn(DecArgs a) {
   flash_store<D>(qi < a.q ? a.out + ((int64_t)r * a.q + qi) * a.h1 + h * D : nullptr, l_lane, o);
 }
 
-// ------------------------------------------------------------ tree masks
-// [SpecPipe] 2.2.1: token i sees itself and its ancestors.  Lane i of a
-// wave holds token i of one request.  The ancestor sets come from pointer
-// jumping over lane shuffles: after round k, m holds the tokens at distance
-// 0 .. 2^k - 1 above token i and a the one at distance 2^k (-1 past the
-// root); six rounds cover any depth below 64.  A token whose own parent
-// entry breaks the rules (ok false) is treated as a root, so a valid token's
-// set stops at, and includes, the first such ancestor.
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
-  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t ancestor_set(int i, int q, int p0, bool ok) {
-  uint64_t m = i < q ? 1ull << i : 0ull;
-  int a = (i < q && ok) ? p0 : -1;
-#pragma unroll
-  for (int k = 0; k < 6; ++k) {
-    const int from = a < 0 ? i : a;  // every lane takes part in the shuffles
-    const uint64_t ma = shfl_u64(m, from);
-    const int aa = __shfl(a, from);
-    if (a >= 0) {
-      m |= ma;
-      a = aa;
-    }
-  }
-  return m;
-}
-
-__device__ __forceinline__ bool parent_ok(int i, int p) {
-  return i == 0 ? p == -1 : (p >= 0 && p < i);
-}
-
-// One wave per request (up to 16 waves, each taking every 16th request); an
-// entry breaking the parent rules keeps only its own bit and is counted.
-__global__ __launch_bounds__(1024) void k_tree_masks(int b, int q, const int32_t* __restrict__ parent,
-                                                     uint64_t* __restrict__ masks,
-                                                     int32_t* __restrict__ err) {
-  __shared__ int bad[16];
-  const int i = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int nbad = 0;
-  for (int r = w; r < b; r += nw) {
-    const int p0 = i < q ? parent[(int64_t)r * q + i] : -1;
-    const bool ok = i >= q || parent_ok(i, p0);
-    nbad += ok ? 0 : 1;
-    const uint64_t m = ancestor_set(i, q, p0, ok);
-    if (i < q) masks[(int64_t)r * q + i] = m;
-  }
-  for (int o = 32; o > 0; o >>= 1) nbad += __shfl_xor(nbad, o);
-  if (i == 0) bad[w] = nbad;
-  __syncthreads();
-  if (threadIdx.x == 0 && err) {
-    int t = 0;
-    for (int j = 0; j < nw; ++j) t += bad[j];
-    *err = t;
-  }
-}
-
-// ------------------------------------------------------------ tree pruning
-// [SpecPipe] 2.2.1 sub-tree pruning (Fig. 5-b) and 2.2.2 (Fig. 8): once
-// token u of a request is verified, the request keeps the tokens on u's path
-// to the root (the verified path, whose cache rows every kept token sees) and
-// u's subtree (the tokens with u as an ancestor), in BFS order.  One wave per
-// request; lane i holds token i: its ancestor set as in k_tree_masks, a
-// ballot of the kept lanes gives each kept token its new index, and a lane
-// shuffle maps its parent to the parent's new index.  Slots past the kept
-// count become filler leaves (the last kept token's parent, or 0 when one
-// token is kept) so the new array stays a valid BFS parent array.  A request
-// with an invalid parent array or verified index keeps nothing and is
-// counted in err.
-__global__ __launch_bounds__(1024) void k_tree_prune(int b, int q, const int32_t* __restrict__ parent,
-                                                     const int32_t* __restrict__ verified,
-                                                     int32_t* __restrict__ new_parent,
-                                                     int32_t* __restrict__ src,
-                                                     int32_t* __restrict__ kept_out,
-                                                     int32_t* __restrict__ err) {
-  __shared__ int bad[16];
-  const int i = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int nbad = 0;
-  for (int r = w; r < b; r += nw) {
-    const int p0 = i < q ? parent[(int64_t)r * q + i] : -1;
-    const bool ok = i >= q || parent_ok(i, p0);
-    const int u = verified[r];
-    const bool good = !__any(!ok) && u >= 0 && u < q;
-    int32_t* npr = new_parent + (int64_t)r * q;
-    int32_t* sr = src + (int64_t)r * q;
-    if (!good) {
-      if (i == 0) {
-        kept_out[r] = 0;
-        ++nbad;
-      }
-      if (i < q) {
-        npr[i] = i == 0 ? -1 : 0;
-        sr[i] = -1;
-      }
-      continue;
-    }
-    const uint64_t m = ancestor_set(i, q, p0, true);
-    const uint64_t mu = shfl_u64(m, u);
-    const bool keep = i < q && (((mu >> i) & 1ull) || ((m >> u) & 1ull));
-    const uint64_t kb = __ballot(keep);
-    const int newidx = __popcll(kb & ((1ull << i) - 1ull));  // kept lanes below i
-    const int kept = __popcll(kb);
-    const int nidx_of_parent = __shfl(newidx, p0 < 0 ? 0 : p0);
-    const int np = p0 < 0 ? -1 : nidx_of_parent;
-    const int last = 63 - __clzll(kb);  // lane of the last kept token
-    const int np_last = __shfl(np, last);
-    const int fill = kept == 1 ? 0 : np_last;
-    if (keep) {
-      npr[newidx] = np;
-      sr[newidx] = i;
-    }
-    if (i < q && i >= kept) {
-      npr[i] = fill;
-      sr[i] = -1;
-    }
-    if (i == 0) kept_out[r] = kept;
-  }
-  if (i == 0) bad[w] = nbad;
-  __syncthreads();
-  if (threadIdx.x == 0 && err) {
-    int t = 0;
-    for (int j = 0; j < nw; ++j) t += bad[j];
-    *err = t;
-  }
-}
-
-// Moves kept tree rows into place after k_tree_prune: one wave per
-// (request, head, K or V); lane j copies the row of kept token j from cache
-// row pos + src[j] to row pos + j (RB bytes of codes or fp16, SMB bytes of
-// scale/min pairs).  Every lane's store depends on its own load and each
-// load instruction covers the whole wave, so all rows are read before any is
-// overwritten.
-template <int RB, int SMB>
-__global__ __launch_bounds__(64) void k_kv_compact(int q, int heads, int pos, int cap,
-                                                   const int32_t* __restrict__ src,
-                                                   const int32_t* __restrict__ kept, uint8_t* k,
-                                                   uint8_t* v, uint8_t* ksm, uint8_t* vsm) {
-  const int j = threadIdx.x;
-  const int t = blockIdx.x & 1, rh = blockIdx.x >> 1;
-  const int h = rh % heads, r = rh / heads;
-  const int n = min(max(kept[r], 0), q);  // any kept / src values stay inside rows [pos, pos + q)
-  const int64_t row0 = (int64_t)(r * heads + h) * cap + pos;
-  uint8_t* base = (t ? v : k) + row0 * RB;
-  uint8_t* sbase = SMB ? (t ? vsm : ksm) + row0 * SMB : nullptr;
-  const int s = j < n ? src[(int64_t)r * q + j] : j;
-  const bool act = j < n && s >= 0 && s < q;
-  u32x4 buf[RB / 16];
-  uint32_t sm[SMB / 4 > 0 ? SMB / 4 : 1];
-  if (act) {
-#pragma unroll
-    for (int c = 0; c < RB / 16; ++c) buf[c] = *(const u32x4*)(base + (int64_t)s * RB + 16 * c);
-#pragma unroll
-    for (int c = 0; c < SMB / 4; ++c) sm[c] = *(const uint32_t*)(sbase + (int64_t)s * SMB + 4 * c);
-  }
-  if (act && s != j) {
-#pragma unroll
-    for (int c = 0; c < RB / 16; ++c) *(u32x4*)(base + (int64_t)j * RB + 16 * c) = buf[c];
-#pragma unroll
-    for (int c = 0; c < SMB / 4; ++c) *(uint32_t*)(sbase + (int64_t)j * SMB + 4 * c) = sm[c];
-  }
-}
-
 // -------------------------------------------------------------- launchers
 void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
                       int32_t pos, const int32_t* dpos, const hp_kv& kv, hipStream_t st) {
@@ -945,42 +573,6 @@ void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, c
     hipLaunchKernelGGL(k_prefill_attn<128>, grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(k_prefill_attn<64>, grid, dim3(256), 0, st, a);
-}
-
-void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
-                       hipStream_t st) {
-  Prof prof("tree_masks", st);
-  hipLaunchKernelGGL(k_tree_masks, dim3(1), dim3(64 * std::min(b, 16)), 0, st, b, q, parent,
-                     masks, err);
-}
-
-void launch_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
-                       int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
-                       hipStream_t st) {
-  Prof prof("tree_prune", st);
-  hipLaunchKernelGGL(k_tree_prune, dim3(1), dim3(64 * std::min(b, 16)), 0, st, b, q, parent,
-                     verified, new_parent, src, kept, err);
-}
-
-void launch_kv_compact(int32_t b, int32_t q, int32_t heads, int32_t d, int32_t pos,
-                       const int32_t* src, const int32_t* kept, const hp_kv& kv, hipStream_t st) {
-  const dim3 grid((unsigned)(2 * b * heads));
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, q, heads, pos, kv.cap, src, kept,
-                       (uint8_t*)kv.k, (uint8_t*)kv.v, (uint8_t*)kv.k_sm, (uint8_t*)kv.v_sm);
-  };
-  Prof prof("kv_compact", st);
-  if (kv.fmt == HP_Q4) {
-    if (d == 128)
-      go(k_kv_compact<64, 8>);
-    else
-      go(k_kv_compact<32, 4>);
-  } else {
-    if (d == 128)
-      go(k_kv_compact<256, 0>);
-    else
-      go(k_kv_compact<128, 0>);
-  }
 }
 
 }  // namespace hp

@@ -211,9 +211,12 @@ static hp_status prefill_body(int b, int s, int h1, int h2, int heads, const hp_
   return layer_tail(w, M, h1, h2, x, x_out, ws, L, st);
 }
 
+// topk_max_t > 0: Top-K sparse attention ([FlexGen] section 5) keeping
+// ceil(T / 10) rows, with T <= topk_max_t (q == 1 only).
 static hp_status decode_body(int b, int q, int h1, int h2, int heads, const hp_layer& w,
                              const void* t, int pos, const int32_t* dpos, const uint64_t* masks,
-                             const hp_kv& kv, void* t_out, void* ws, const Ws& L, hipStream_t st) {
+                             const hp_kv& kv, void* t_out, void* ws, const Ws& L, hipStream_t st,
+                             int topk_max_t = 0) {
   const int64_t M = (int64_t)b * q;
   _Float16* qkv = at<_Float16>(ws, L.qkv);
   hp_status r;
@@ -222,8 +225,15 @@ static hp_status decode_body(int b, int q, int h1, int h2, int heads, const hp_l
     return r;
   launch_kv_append(b, q, h1, heads, qkv, pos, dpos, kv, st);
   if ((r = launch_ok("k_kv_append")) != HP_OK) return r;
-  launch_decode_attention(b, q, h1, heads, qkv, pos, dpos, masks, kv, at<void>(ws, L.a), st);
-  if ((r = launch_ok("k_decode_attn")) != HP_OK) return r;
+  if (topk_max_t > 0) {
+    if ((r = launch_topk_attention(b, h1, heads, qkv, pos, dpos, topk_max_t, 0, kv,
+                                   at<void>(ws, L.a), nullptr, st)) != HP_OK)
+      return fail(r, "topk attention: bad row count");
+    if ((r = launch_ok("k_topk_attn")) != HP_OK) return r;
+  } else {
+    launch_decode_attention(b, q, h1, heads, qkv, pos, dpos, masks, kv, at<void>(ws, L.a), st);
+    if ((r = launch_ok("k_decode_attn")) != HP_OK) return r;
+  }
   return layer_tail(w, M, h1, h2, t, t_out, ws, L, st);
 }
 
@@ -414,6 +424,25 @@ hp_status hp_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, c
   return launch_ok("k_decode_attn");
 }
 
+hp_status hp_topk_attention(int32_t b, int32_t h1, int32_t heads, const void* qkv, int32_t pos,
+                            int32_t topk, const hp_kv* kv, void* out, int32_t* idx, void* stream) {
+  if (b <= 0 || h1 <= 0 || heads <= 0 || h1 % heads || pos < 0) return fail(HP_ERR_SHAPE, "bad sizes");
+  const int D = h1 / heads;
+  if (D != 64 && D != 128) return fail(HP_ERR_SHAPE, "head dim %d not in {64, 128}", D);
+  if (pos + 1 > 4096) return fail(HP_ERR_SHAPE, "pos + 1 = %d rows exceeds 4096", pos + 1);
+  if (topk < 0) return fail(HP_ERR_SHAPE, "topk must be >= 0");
+  if (!qkv || !out) return fail(HP_ERR_NULL, "NULL pointer");
+  NEED_ALIGN(qkv, 16);
+  NEED_ALIGN(out, 16);
+  hp_status s = check_kv(kv, pos + 1);
+  if (s != HP_OK) return s;
+  if ((s = device_check()) != HP_OK) return s;
+  if ((s = launch_topk_attention(b, h1, heads, qkv, pos, nullptr, pos + 1, topk, *kv, out, idx,
+                                 S(stream))) != HP_OK)
+    return fail(s, "topk attention: bad row count");
+  return launch_ok("k_topk_attn");
+}
+
 hp_status hp_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
                         void* stream) {
   if (b <= 0) return fail(HP_ERR_SHAPE, "b must be positive");
@@ -538,6 +567,8 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   if (ws_bytes < L.total) return fail(HP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   const bool rbr = flags & HP_ROW_BY_ROW, mb = flags & HP_MICROBATCH;
   const bool graph = (flags & HP_GRAPH) && !rbr;
+  const int topk_max_t = (flags & HP_TOPK10) ? d->s + d->n : 0;
+  if (topk_max_t > 4096) return fail(HP_ERR_SHAPE, "HP_TOPK10 needs s + n <= 4096");
   if (graph && !stream) return fail(HP_ERR_SHAPE, "HP_GRAPH needs a non-default stream");
   if ((s = device_check()) != HP_OK) return s;
   hipStream_t st = S(stream);
@@ -563,7 +594,8 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
     const _Float16* in = (j % 2 == 0) ? T0 : T1;
     _Float16* out = (j % 2 == 0) ? T1 : T0;
     return decode_body(nb, 1, d->h1, d->h2, d->heads, layers[j], in + r0 * h1, d->s, dstep,
-                       nullptr, kv_slice(kv[j], d->heads, D, r0), out + r0 * h1, ws, L, st);
+                       nullptr, kv_slice(kv[j], d->heads, D, r0), out + r0 * h1, ws, L, st,
+                       topk_max_t);
   };
   auto stage_in = [&](int64_t r0, int nb) {
     launch_copy_step((const _Float16*)t_in + r0 * h1, nb * h1, bh, dstep, T0 + r0 * h1, 0, st);

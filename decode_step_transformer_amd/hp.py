@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhp.so")
 
 HP_F16, HP_Q4 = 0, 1
-HP_GRAPH, HP_ROW_BY_ROW, HP_MICROBATCH = 1, 2, 4
+HP_GRAPH, HP_ROW_BY_ROW, HP_MICROBATCH, HP_TOPK10 = 1, 2, 4, 8
 
 
 class HPError(RuntimeError):
@@ -47,7 +47,8 @@ class hp_dims(C.Structure):
 EXPORTS = [
     "hp_last_error", "hp_device_check", "hp_quantize_g64", "hp_dequantize_g64",
     "hp_pack_weight_q4", "hp_pack_weight_f16", "hp_gemm_workspace_bytes", "hp_gemm",
-    "hp_kv_append", "hp_prefill_attention", "hp_decode_attention", "hp_tree_masks",
+    "hp_kv_append", "hp_prefill_attention", "hp_decode_attention", "hp_topk_attention",
+    "hp_tree_masks",
     "hp_tree_prune", "hp_kv_compact",
     "hp_workspace_bytes", "hp_layer_prefill", "hp_layer_decode", "hp_run_block",
     "hp_release_graphs", "hp_weight_bytes", "hp_kv_bytes", "hp_profile", "hp_profile_read",
@@ -75,6 +76,7 @@ def lib():
             "hp_kv_append": [_i32, _i32, _i32, _i32, _p, _i32, C.POINTER(hp_kv), _p],
             "hp_prefill_attention": [_i32, _i32, _i32, _i32, _p, _p, _p],
             "hp_decode_attention": [_i32, _i32, _i32, _i32, _p, _i32, _p, C.POINTER(hp_kv), _p, _p],
+            "hp_topk_attention": [_i32, _i32, _i32, _p, _i32, _i32, C.POINTER(hp_kv), _p, _p, _p],
             "hp_tree_masks": [_i32, _i32, _p, _p, _p, _p],
             "hp_tree_prune": [_i32, _i32, _p, _p, _p, _p, _p, _p, _p],
             "hp_kv_compact": [_i32, _i32, _i32, _i32, _i32, _p, _p, C.POINTER(hp_kv), _p],
@@ -256,6 +258,20 @@ def hp_decode_attention(b, q, h1, heads, qkv, pos, kv: KVCache, masks=None, out=
     _check(lib().hp_decode_attention(b, q, h1, heads, _ptr(qkv), pos, _ptr(masks), C.byref(c),
                                      _ptr(out), _stream(stream)))
     return out
+
+
+def hp_topk_attention(b, h1, heads, qkv, pos, kv: KVCache, topk=0, out=None, idx=False,
+                      stream=None):
+    """Top-K sparse decode attention; returns out [b][h1], or (out, idx [b][heads][K])
+    when idx is True (K = topk, at most pos + 1, or ceil((pos + 1) / 10) for topk 0)."""
+    out = out if out is not None else torch.empty((b, h1), dtype=torch.float16, device=qkv.device)
+    T = pos + 1
+    K = min(topk, T) if topk > 0 else -(-T // 10)
+    ix = torch.empty((b, heads, K), dtype=torch.int32, device=qkv.device) if idx else None
+    c = kv.c()
+    _check(lib().hp_topk_attention(b, h1, heads, _ptr(qkv), pos, topk, C.byref(c), _ptr(out),
+                                   _ptr(ix), _stream(stream)))
+    return (out, ix) if idx else out
 
 
 def hp_tree_masks(parent: torch.Tensor, stream=None):

@@ -24,7 +24,8 @@ block's prefill column issues one such call per layer (all GPU batches in one
 launch), so its GEMM launches have the block's shapes.  `decode` runs one
 layer decode the same way, at the cache length where bench.py times the
 decode kernels (the decode GEMM and attention; select them with
---kernel-include-regex 'k_gemm_dq|k_decode_attn').
+--kernel-include-regex 'k_gemm_dq|k_decode_attn').  `topk` runs Top-K sparse
+attention at the same cache length (k_topk_attn).
 
 `summarize` writes profiles/traffic.json: per kernel, the calibrated bytes
 read and written per dispatch and a hash of the sources that define the
@@ -48,7 +49,8 @@ COPY_BYTES = 1 << 30
 KERNEL_SOURCES = {
     "k_gemm16": ["csrc/gemm16.hip", "csrc/lds_dma.h", "csrc/common.h"],
     "k_gemm_dq": ["csrc/gemm_dec.hip", "csrc/lds_dma.h", "csrc/dequant_dev.h", "csrc/common.h"],
-    "k_decode_attn": ["csrc/attn.hip", "csrc/dequant_dev.h", "csrc/common.h"],
+    "k_decode_attn": ["csrc/attn.hip", "csrc/decode_dev.h", "csrc/dequant_dev.h", "csrc/common.h"],
+    "k_topk_attn": ["csrc/topk.hip", "csrc/decode_dev.h", "csrc/dequant_dev.h", "csrc/common.h"],
 }
 
 
@@ -126,6 +128,22 @@ def decode(config: str, calls: int = 2) -> None:
         print(f"decode call {i} done", flush=True)
 
 
+def topk(config: str, calls: int = 2) -> None:
+    """One prefill, then `calls` eager Top-K sparse attention calls at cache length
+    s + n/2 (the sparse_attention timing point of bench.py)."""
+    import torch
+
+    n = _config_n(config)
+    hp, c, d, layer, x, kv, ws, out = _one_layer(config, n)
+    hp.hp_layer_prefill(d, layer, x, kv, out, ws)
+    qkv = torch.randn((c["b"], 3 * c["h1"]), device="cuda").half()
+    pos = c["s"] + n // 2 - 1
+    for i in range(calls):
+        hp.hp_topk_attention(c["b"], c["h1"], c["heads"], qkv, pos, kv)
+        torch.cuda.synchronize()
+        print(f"topk call {i} done", flush=True)
+
+
 def _config_n(config: str) -> int:
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
@@ -189,6 +207,8 @@ if __name__ == "__main__":
         prefill(sys.argv[2])
     elif len(sys.argv) == 3 and sys.argv[1] == "decode":
         decode(sys.argv[2])
+    elif len(sys.argv) == 3 and sys.argv[1] == "topk":
+        topk(sys.argv[2])
     elif len(sys.argv) == 8 and sys.argv[1] == "summarize":
         print(json.dumps(summarize(*sys.argv[2:8]), indent=1))
     else:

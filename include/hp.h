@@ -189,6 +189,19 @@ hp_status hp_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, c
                               int32_t pos, const uint64_t* masks, const hp_kv* kv, void* out,
                               void* stream);
 
+/* Top-K sparse decode attention ([FlexGen] section 5, sparse attention): for
+ * request r's new token (its K/V already appended at row pos), the scores
+ * q . k_j over cache rows j in [0, pos] are formed through the stored format,
+ * the K largest are kept (ties to the lower row), the other rows are dropped
+ * and the output is the attention over the kept rows only (softmax over
+ * them; only their V rows are read).  K = topk (at most pos + 1), or
+ * ceil((pos + 1) / 10) when topk == 0.  qkv: device half [b][3 h1] (query in
+ * columns [0, h1)); out: device half [b][h1]; idx: device int32
+ * [b][heads][K] receiving the kept rows in ascending order, or NULL.
+ * Requires pos + 1 <= min(kv->cap, 4096). */
+hp_status hp_topk_attention(int32_t b, int32_t h1, int32_t heads, const void* qkv, int32_t pos,
+                            int32_t topk, const hp_kv* kv, void* out, int32_t* idx, void* stream);
+
 /* [SpecPipe] 2.2.1 (tree mask M): builds masks[r][i] (bit u set iff token u
  * is token i or one of its ancestors) from a BFS parent array per request:
  * parent: device int32 [b][q], parent[r][0] == -1 and
@@ -247,8 +260,11 @@ hp_status hp_layer_decode(const hp_dims* d, const hp_layer* w, const void* t, in
 enum {
   HP_GRAPH = 1,      /* capture one decode column as a hipGraph, replay it n times */
   HP_ROW_BY_ROW = 2, /* row-by-row order: each GPU batch runs all steps alone */
-  HP_MICROBATCH = 4  /* zig-zag with one launch per GPU batch (gbs rows)
+  HP_MICROBATCH = 4, /* zig-zag with one launch per GPU batch (gbs rows)
                         instead of one launch per block */
+  HP_TOPK10 = 8      /* decode columns use Top-K sparse attention keeping
+                        ceil(T / 10) of the T visible rows ([FlexGen] section 5,
+                        sparse attention; see hp_topk_attention); s + n <= 4096 */
 };
 
 /* [FlexGen] section 4, Algorithm 1: zig-zag block schedule over one block of

@@ -279,6 +279,50 @@ def layer_decode(t, W, kv: KV, heads: int, pos: int, masks=None) -> np.ndarray:
     return y.view(np.float16)
 
 
+def layer_decode_topk(t, W, kv: KV, heads: int, pos: int, topk: int = 0) -> np.ndarray:
+    """The decode step of layer_decode (one new token per request, t[b][1][h1] at cache
+    row pos) with the Top-K sparse attention of [FlexGen] section 5 in place of the
+    attention: K = topk (at most pos + 1) kept rows per (request, head), or
+    ceil((pos + 1) / 10) for topk 0.  Same steps and fp16 rounding points as
+    layer_decode: Q, K, V products, append, attention, then the output projection with
+    the residual and the ReLU MLP with the residual."""
+    tb = _bits(t)
+    b, nq, h1 = tb.shape
+    assert nq == 1
+    d = h1 // heads
+    x = tb.reshape(b, h1)
+    q, k, v = gemm(x, W["wq"]), gemm(x, W["wk"]), gemm(x, W["wv"])
+    kv_append(kv, k.reshape(b, 1, h1), v.reshape(b, 1, h1), pos)
+    T = pos + 1
+    K = min(topk, T) if topk > 0 else topk_count(T)
+    Kc, Vc = kv.values("k", T), kv.values("v", T)
+    a = np.empty((b, h1), np.float16)
+    for r in range(b):
+        for h in range(heads):
+            cols = slice(h * d, (h + 1) * d)
+            a[r, cols] = topk_attention(q[r, cols], Kc[r, h], Vc[r, h], K)[0]
+    x_out = gemm(a, W["wo"], res=x)
+    hid = gemm(x_out, W["w1"], relu=True)
+    return gemm(hid, W["w2"], res=x_out).reshape(b, 1, h1)
+
+
+def run_block_topk(x, t_in, layers, kvs, heads: int, topk: int = 0):
+    """run_block (zig-zag order; requests never interact, so the order does not change
+    the result) with layer_decode_topk in every decode column."""
+    b, s, h1 = _bits(x).shape
+    n = _bits(t_in).shape[0]
+    cur = np.asarray(x)
+    for j, W in enumerate(layers):
+        cur = layer_prefill(cur, W, kvs[j], heads)
+    t_out = np.empty((n, b, h1), np.float16)
+    for i in range(n):
+        tcur = np.asarray(t_in)[i].reshape(b, 1, h1)
+        for j, W in enumerate(layers):
+            tcur = layer_decode_topk(tcur, W, kvs[j], heads, s + i, topk)
+        t_out[i] = tcur.reshape(b, h1)
+    return cur, t_out
+
+
 def run_block(x, t_in, layers, kvs, heads: int, gbs: int, order: int = 0):
     """Whole block: prefill column then n decode columns over all layers.
 

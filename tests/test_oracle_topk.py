@@ -95,3 +95,66 @@ def test_dropped_tokens_do_not_matter(orc):
 
 def test_topk_count(orc):
     assert [orc.topk_count(T) for T in (1, 9, 10, 11, 528, 2112)] == [1, 1, 1, 2, 53, 212]
+
+
+def _tiny_layer(cid, h1, h2):
+    sh = {"wq": (h1, h1), "wk": (h1, h1), "wv": (h1, h1), "wo": (h1, h1), "w1": (h1, h2),
+          "w2": (h2, h1)}
+    return {k: synth.normal_f16(SEED, 900 + 10 * cid + i, v, 0.05) for i, (k, v) in enumerate(sh.items())}
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_layer_decode_topk_all_rows_is_layer_decode(orc, fmt):
+    """With every row kept, the composed sparse decode step is the oracle's
+    dense decode step bit for bit (outputs and the appended cache rows)."""
+    b, s, h1, h2, heads = 2, 9, 128, 256, 2
+    W = _tiny_layer(0, h1, h2)
+    x = synth.normal_f16(SEED, 950, (b, s, h1))
+    t = synth.normal_f16(SEED, 951, (b, 1, h1))
+    kva, kvb = (orc.KV(fmt, b, heads, s + 1, h1 // heads) for _ in range(2))
+    orc.layer_prefill(x, W, kva, heads)
+    orc.layer_prefill(x, W, kvb, heads)
+    ya = orc.layer_decode_topk(t, W, kva, heads, s, topk=10 ** 6)
+    yb = orc.layer_decode(t, W, kvb, heads, s)
+    assert np.array_equal(ya.view(np.uint16), yb.view(np.uint16))
+    assert np.array_equal(kva.k, kvb.k) and np.array_equal(kva.v, kvb.v)
+
+
+def test_run_block_topk_all_rows_is_run_block(orc):
+    b, s, n, h1, h2, heads, l = 2, 6, 3, 128, 256, 2, 2
+    Ws = [_tiny_layer(j, h1, h2) for j in range(l)]
+    x = synth.normal_f16(SEED, 960, (b, s, h1))
+    t = synth.normal_f16(SEED, 961, (n, b, h1))
+    ka = [orc.KV(1, b, heads, s + n, h1 // heads) for _ in range(l)]
+    kb = [orc.KV(1, b, heads, s + n, h1 // heads) for _ in range(l)]
+    xa, ta = orc.run_block_topk(x, t, Ws, ka, heads, topk=10 ** 6)
+    xb, tb = orc.run_block(x, t, Ws, kb, heads, b)
+    assert np.array_equal(xa.view(np.uint16), xb.view(np.uint16))
+    assert np.array_equal(ta.view(np.uint16), tb.view(np.uint16))
+
+
+def test_layer_decode_topk_uses_kept_rows_only(orc):
+    """With K < T, the step's attention output changes only through the kept
+    rows: perturbing a dropped row's V leaves the output bitwise unchanged."""
+    b, s, h1, h2, heads = 1, 40, 128, 256, 2
+    W = _tiny_layer(1, h1, h2)
+    x = synth.normal_f16(SEED, 970, (b, s, h1))
+    t = synth.normal_f16(SEED, 971, (b, 1, h1))
+    kva, kvb = (orc.KV(0, b, heads, s + 1, h1 // heads) for _ in range(2))
+    orc.layer_prefill(x, W, kva, heads)
+    orc.layer_prefill(x, W, kvb, heads)
+    # the kept rows of head 0 and 1 (same query as the step will form)
+    q = orc.gemm(t.reshape(b, h1), W["wq"])
+    kn = orc.gemm(t.reshape(b, h1), W["wk"])
+    K = orc.topk_count(s + 1)
+    d = h1 // heads
+    keys = np.concatenate([kva.values("k", s)[0], kn.reshape(1, heads, 1, d).repeat(1, 0)[0]], axis=1)
+    kept = set()
+    for h in range(heads):
+        z = keys[h].astype(np.float64) @ q[0, h * d:(h + 1) * d].astype(np.float64)
+        kept |= {int(j) for j in np.argsort(-z, kind="stable")[:K]}
+    row = next(j for j in range(s) if j not in kept)
+    kvb.v[0, :, row] = np.float16(7.0).view(np.uint16)
+    ya = orc.layer_decode_topk(t, W, kva, heads, s)
+    yb = orc.layer_decode_topk(t, W, kvb, heads, s)
+    assert np.array_equal(ya.view(np.uint16), yb.view(np.uint16))
