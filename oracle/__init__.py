@@ -326,9 +326,9 @@ def run_block_topk(x, t_in, layers, kvs, heads: int, topk: int = 0):
 def run_block(x, t_in, layers, kvs, heads: int, gbs: int, order: int = 0):
     """Whole block: prefill column then n decode columns over all layers.
 
-    layers: list of dicts of fp16 weights; kvs: list of KV; order 0 zig-zag, 1 row-by-row.
-    Returns (x_out[b][s][h1], t_out[n][b][h1]).
-    """
+    layers: list of dicts of fp16 weights; kvs: list of KV; order 0 zig-zag, 1 row-by-row,
+    2 diagonal (the KV arrays then need only min(b/gbs, n+1) GPU batches of requests).
+    Returns (x_out[b][s][h1], t_out[n][b][h1])."""
     xb, tb = _bits(x), _bits(t_in)
     b, s, h1 = xb.shape
     n = tb.shape[0]

@@ -27,6 +27,7 @@
 //
 // Parity pins: tests/test_oracle_*.py check every function here against values
 // and identities fixed by the pages and by mathematics (see each function).
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -441,8 +442,14 @@ int or_tree_prune(const int32_t* parent, int nq, int u, int32_t* new_parent, int
 // column, steps 1..n are decode columns.  order 0 is the zig-zag block
 // schedule: for step i, for layer j, for GPU batch k.  order 1 is the
 // row-by-row schedule of the baseline systems: for GPU batch k, for step i,
-// for layer j.  Each layer's K/V cache lives in kv_k[j], kv_v[j] (and the
-// sm arrays for int4).  Inputs: x[b][s][h1] (prompt embeddings) and
+// for layer j.  order 2 is the diagonal block schedule ([FlexGen] appendix
+// A.2, Fig. 5): GPU batch k starts one iteration after batch k - 1, so at
+// iteration it batch k is at step it - k (0 <= it - k <= n); each iteration
+// runs layer 0 for every batch on that diagonal, then layer 1, and so on.
+// Each layer's K/V cache lives in kv_k[j], kv_v[j] (and the sm arrays for
+// int4); under order 2 a batch needs its cache only from its prefill to its
+// last step, so batch k uses cache slot k mod min(nb, n + 1) (the arrays hold
+// that many GPU batches).  Inputs: x[b][s][h1] (prompt embeddings) and
 // t_in[n][b][h1] (one embedding per decode step: the pages define no token
 // sampling, so each decode step is fed a given embedding).  Outputs: the last
 // layer's prefill activations x_out[b][s][h1] and decode outputs
@@ -459,12 +466,14 @@ void or_run_block(int b, int s, int n, int h1, int h2, int l, int heads, int gbs
   const i64 req_rows = (i64)heads * cap;
   // per-micro-batch activations (prefill and decode)
   std::vector<std::vector<uint16_t>> xa(nb), ta(nb);
+  const int nslot = order == 2 ? std::min(nb, n + 1) : nb;
   auto run = [&](int i, int j, int k) {
     const i64 r0 = (i64)k * gbs;
-    void* kk = (uint8_t*)kv_k[j] + r0 * req_rows * code_row;
-    void* vv = (uint8_t*)kv_v[j] + r0 * req_rows * code_row;
-    uint16_t* ks = kv_fmt == OR_F16 ? nullptr : k_sm[j] + r0 * req_rows * sm_row;
-    uint16_t* vs = kv_fmt == OR_F16 ? nullptr : v_sm[j] + r0 * req_rows * sm_row;
+    const i64 c0 = (i64)(k % nslot) * gbs;  // first request of this batch's cache slot
+    void* kk = (uint8_t*)kv_k[j] + c0 * req_rows * code_row;
+    void* vv = (uint8_t*)kv_v[j] + c0 * req_rows * code_row;
+    uint16_t* ks = kv_fmt == OR_F16 ? nullptr : k_sm[j] + c0 * req_rows * sm_row;
+    uint16_t* vs = kv_fmt == OR_F16 ? nullptr : v_sm[j] + c0 * req_rows * sm_row;
     const uint16_t* const* W = w + 6 * j;
     if (i == 0) {
       std::vector<uint16_t>& cur = xa[k];
@@ -490,6 +499,10 @@ void or_run_block(int b, int s, int n, int h1, int h2, int l, int heads, int gbs
     for (int i = 0; i <= n; ++i)
       for (int j = 0; j < l; ++j)
         for (int k = 0; k < nb; ++k) run(i, j, k);
+  } else if (order == 2) {
+    for (int it = 0; it < nb + n; ++it)
+      for (int j = 0; j < l; ++j)
+        for (int k = std::max(0, it - n); k <= std::min(it, nb - 1); ++k) run(it - k, j, k);
   } else {
     for (int k = 0; k < nb; ++k)
       for (int i = 0; i <= n; ++i)

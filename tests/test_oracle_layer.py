@@ -245,6 +245,56 @@ def test_schedule_invariance(orc, fmt):
                 assert np.array_equal(a, c)
 
 
+def _diagonal_cells(nb, n):
+    """[FlexGen] appendix A.2, Fig. 5, as read here: the iterations of the diagonal
+    block schedule, each a list of (GPU batch, step) cells (step 0 is the prefill)."""
+    its = []
+    for it in range(nb + n):
+        its.append([(k, it - k) for k in range(nb) if 0 <= it - k <= n])
+    return its
+
+
+@pytest.mark.parametrize("nb,n", [(1, 3), (2, 8), (4, 2), (6, 3), (40, 8)])
+def test_diagonal_schedule_cells(nb, n):
+    """Every (batch, step) cell runs exactly once, a batch's steps run in order in
+    consecutive iterations, and in steady state an iteration holds one batch at
+    every step 0..n: n decode cells, so gbs * n tokens per weight load, the same
+    weight reads per token as a zig-zag block of gbs * n requests (the page's
+    statement); at most n + 1 batches are live at once, the cache slots needed."""
+    its = _diagonal_cells(nb, n)
+    cells = [c for it in its for c in it]
+    assert sorted(cells) == [(k, i) for k in range(nb) for i in range(n + 1)]
+    for k in range(nb):
+        when = [t for t, it in enumerate(its) for (kk, i) in it if kk == k]
+        assert when == list(range(k, k + n + 1))
+    assert max(len(it) for it in its) == min(nb, n + 1)
+    for it in its[n:nb]:  # steady state (exists when nb > n)
+        assert sorted(i for _, i in it) == list(range(n + 1))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("b,gbs,n", [(4, 1, 2), (6, 1, 3), (4, 2, 3), (4, 4, 2)])
+def test_diagonal_schedule_equals_zigzag(orc, fmt, b, gbs, n):
+    """The diagonal order (cache slots reused: the KV arrays hold only min(b/gbs, n+1)
+    GPU batches) gives the zig-zag block's outputs bit for bit: requests never
+    interact, so only the order of the cells changes."""
+    rng = np.random.default_rng(31 + b + n)
+    s, h1, h2, l, H = 5, 128, 128, 2, 2
+    layers = [weights(rng, h1, h2) for _ in range(l)]
+    x = f16(rng, (b, s, h1))
+    t = f16(rng, (n, b, h1))
+    kz = [orc.KV(fmt, b, H, s + n, h1 // H) for _ in range(l)]
+    xz, tz = orc.run_block(x, t, layers, kz, H, gbs, 0)
+    slots = min(b // gbs, n + 1) * gbs
+    kd = [orc.KV(fmt, slots, H, s + n, h1 // H) for _ in range(l)]
+    xd, td = orc.run_block(x, t, layers, kd, H, gbs, 2)
+    assert np.array_equal(xd.view(np.uint16), xz.view(np.uint16))
+    assert np.array_equal(td.view(np.uint16), tz.view(np.uint16))
+    last = (b // gbs - 1) % (slots // gbs)  # the slot of the last batch holds its cache
+    for j in range(l):
+        assert np.array_equal(kd[j].k[last * gbs:(last + 1) * gbs], kz[j].k[b - gbs:])
+
+
 def test_block_equals_layer_composition(orc):
     rng = np.random.default_rng(30)
     b, s, n, h1, h2, l, H = 2, 5, 2, 128, 128, 2, 2
