@@ -24,6 +24,8 @@ Prints one JSON line (rank 0, N = 1 only):
                    dense decode attention at the decode shape;
   topk10_block  -- one more block with Top-K sparse attention in its decode
                    columns (decode tokens/s), unless --no-topk-block;
+  diagonal_block-- the timed block's requests under the diagonal block
+                   schedule (whole-schedule time), unless --no-diagonal;
   tree_attention-- the tree-masked decode attention workload (8 requests,
                    2048-row int4 prefix, 64 tree tokens), event-timed, with the
                    pruning plan and cache compaction after verification;
@@ -345,6 +347,8 @@ def main():
     ap.add_argument("--no-tree", action="store_true", help="skip the tree-attention workload")
     ap.add_argument("--no-topk-block", action="store_true",
                     help="skip the extra block with Top-K sparse decode attention")
+    ap.add_argument("--no-diagonal", action="store_true",
+                    help="skip the extra run of the block under the diagonal schedule")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; each GPU would run its own block "
@@ -416,6 +420,16 @@ def main():
                           "tokens_per_s": c["b"] * c["n"] / (tk[1] / 1e3),
                           "work": "one block as timed above (second run, graph cached) with "
                                   "HP_TOPK10: ceil(T/10) rows per (request, head) in decode"}
+        diag = None
+        if not args.no_diagonal:
+            # the same requests under the diagonal block schedule (eager launches;
+            # prefill and decode interleave, so only the whole schedule is timed)
+            nslot = min(c["b"] // c["gbs"], c["n"] + 1)
+            td = hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws, hp.HP_DIAGONAL,
+                                 timing=True, stream=stream)
+            diag = {"total_ms": td[1], "kv_slots": nslot,
+                    "kv_GB": nslot * c["gbs"] / c["b"] * kvbytes / 1e9,
+                    "iterations": c["b"] // c["gbs"] + c["n"]}
         tree = None if args.no_tree else tree_attention(hp, torch, stream)
 
     b, n, s, l = c["b"], c["n"], c["s"], c["l"]
@@ -493,6 +507,11 @@ def main():
         "decode_gemm": dgemm,
         "sparse_attention": sparse,
         "topk10_block": topk_block,
+        "diagonal_block": None if diag is None else dict(
+            diag, tokens_per_s_incl_prefill=b * n / (diag["total_ms"] / 1e3),
+            zigzag_total_ms=pre_ms + dec_ms,
+            work="the timed block's requests under HP_DIAGONAL: GPU batch k runs step it - k "
+                 "of iteration it, weights read once per layer per iteration"),
         "tree_attention": tree,
         "kernels": {k: {"launches": v[0], "total_ms": v[1]} for k, v in prof.items()},
     }

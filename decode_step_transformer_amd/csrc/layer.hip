@@ -253,6 +253,42 @@ static hp_kv kv_slice(const hp_kv& kv, int heads, int D, int64_t r0) {
   return o;
 }
 
+// Layer of the decode cells of one diagonal ([FlexGen] appendix A.2): GPU
+// batches c = 0..nbat-1 of gbs requests each, rows contiguous in t / t_out,
+// batch c at cache row pos[c] of cache slot slot[c].  One QKV product and one
+// tail for all of them (each weight matrix read once), append and attention
+// per batch.
+static hp_status decode_cells(int gbs, int nbat, const int* pos, const int* slot, int h1, int h2,
+                              int heads, const hp_layer& w, const void* t, const hp_kv& kv,
+                              void* t_out, void* ws, const Ws& L, hipStream_t st,
+                              int topk_max_t) {
+  const int64_t M = (int64_t)gbs * nbat;
+  const int D = h1 / heads;
+  _Float16* qkv = at<_Float16>(ws, L.qkv);
+  _Float16* att = at<_Float16>(ws, L.a);
+  hp_status r;
+  if ((r = launch_gemm(t, h1, w.wqkv, M, nullptr, 0, false, qkv, 3 * h1, at<void>(ws, L.part), st)) !=
+      HP_OK)
+    return r;
+  for (int c = 0; c < nbat; ++c) {
+    const _Float16* qc = qkv + (int64_t)c * gbs * 3 * h1;
+    const hp_kv kc = kv_slice(kv, heads, D, (int64_t)slot[c] * gbs);
+    launch_kv_append(gbs, 1, h1, heads, qc, pos[c], nullptr, kc, st);
+    if ((r = launch_ok("k_kv_append")) != HP_OK) return r;
+    _Float16* ac = att + (int64_t)c * gbs * h1;
+    if (topk_max_t > 0) {
+      if ((r = launch_topk_attention(gbs, h1, heads, qc, pos[c], nullptr, topk_max_t, 0, kc, ac,
+                                     nullptr, st)) != HP_OK)
+        return fail(r, "topk attention: bad row count");
+      if ((r = launch_ok("k_topk_attn")) != HP_OK) return r;
+    } else {
+      launch_decode_attention(gbs, 1, h1, heads, qc, pos[c], nullptr, nullptr, kc, ac, st);
+      if ((r = launch_ok("k_decode_attn")) != HP_OK) return r;
+    }
+  }
+  return layer_tail(w, M, h1, h2, t, t_out, ws, L, st);
+}
+
 // -------------------------------------------------------------- profiling
 static std::mutex g_pmu;
 static bool g_prof = false;
@@ -569,6 +605,9 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   const bool graph = (flags & HP_GRAPH) && !rbr;
   const int topk_max_t = (flags & HP_TOPK10) ? d->s + d->n : 0;
   if (topk_max_t > 4096) return fail(HP_ERR_SHAPE, "HP_TOPK10 needs s + n <= 4096");
+  const bool diag = flags & HP_DIAGONAL;
+  if (diag && (flags & (HP_GRAPH | HP_ROW_BY_ROW | HP_MICROBATCH)))
+    return fail(HP_ERR_SHAPE, "HP_DIAGONAL takes no HP_GRAPH, HP_ROW_BY_ROW or HP_MICROBATCH");
   if (graph && !stream) return fail(HP_ERR_SHAPE, "HP_GRAPH needs a non-default stream");
   if ((s = device_check()) != HP_OK) return s;
   hipStream_t st = S(stream);
@@ -582,12 +621,13 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
 
   // layer j of the prefill column for requests [r0, r0 + nb): activations
   // alternate between xb and x_out so that the last layer lands in x_out
-  auto prefill_layer = [&](int j, int64_t r0, int nb) {
+  // (cache rows of requests [c0, c0 + nb); c0 = r0 except under HP_DIAGONAL)
+  auto prefill_layer = [&](int j, int64_t r0, int nb, int64_t c0) {
     const _Float16* in = (j == 0) ? (const _Float16*)x
                                   : (((d->l - j) % 2 == 0) ? (const _Float16*)x_out : xb);
     _Float16* out = ((d->l - 1 - j) % 2 == 0) ? (_Float16*)x_out : xb;
     return prefill_body(nb, d->s, d->h1, d->h2, d->heads, layers[j], in + r0 * sh,
-                        kv_slice(kv[j], d->heads, D, r0), out + r0 * sh, ws, L, st);
+                        kv_slice(kv[j], d->heads, D, c0), out + r0 * sh, ws, L, st);
   };
   // layer j of a decode column: T0 -> T1 -> T0 ...; cache rows at s + *dstep
   auto decode_layer = [&](int j, int64_t r0, int nb) {
@@ -639,7 +679,7 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
     for (int k = 0; k < nbat; ++k) {
       const int64_t r0 = (int64_t)k * d->gbs;
       for (int j = 0; j < d->l; ++j)
-        if ((s = prefill_layer(j, r0, d->gbs)) != HP_OK) return finish(s);
+        if ((s = prefill_layer(j, r0, d->gbs, r0)) != HP_OK) return finish(s);
       launch_set_i32(dstep, 0, false, st);
       for (int i = 0; i < d->n; ++i) {
         if ((s = stage_in(r0, d->gbs)) != HP_OK) return finish(s);
@@ -651,6 +691,53 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
     return finish(launch_ok("row-by-row"));
   }
 
+  if (diag) {
+    // diagonal block schedule ([FlexGen] appendix A.2, Fig. 5): GPU batch k
+    // runs step it - k in iteration it (0: prefill, 1..n: decode); each
+    // iteration takes layer 0 for every batch on its diagonal, then layer 1,
+    // and so on.  Batch k keeps its cache in slot k mod min(nb, n + 1) from its
+    // prefill to its last step.  Prefill and decode interleave: times_ms[0]
+    // is 0 and times_ms[1] the whole schedule.
+    if (times_ms) hipEventRecord(ev[1], st);
+    const int nslot = std::min(nbat, d->n + 1);
+    std::vector<int> pos((size_t)nbat), slot((size_t)nbat);
+    const int64_t gh = (int64_t)d->gbs * h1;
+    const _Float16* last = (d->l % 2 == 1) ? T1 : T0;
+    for (int it = 0; it < nbat + d->n; ++it) {
+      const int dlo = std::max(0, it - d->n), dhi = std::min(it - 1, nbat - 1);  // decode cells
+      const int nd = dhi - dlo + 1;
+      for (int k = dlo; k <= dhi; ++k) {  // batch k at step it - k reads t_in[it - k - 1]
+        pos[k - dlo] = d->s + (it - k) - 1;
+        slot[k - dlo] = k % nslot;
+        const _Float16* src = (const _Float16*)t_in + ((int64_t)(it - k - 1) * d->b) * h1 + k * gh;
+        if ((s = hip_ok(hipMemcpyAsync(T0 + k * gh, src, gh * 2, hipMemcpyDeviceToDevice, st),
+                        "hipMemcpyAsync")) != HP_OK)
+          return finish(s);
+      }
+      for (int j = 0; j < d->l; ++j) {
+        if (it < nbat &&
+            (s = prefill_layer(j, (int64_t)it * d->gbs, d->gbs, (int64_t)(it % nslot) * d->gbs)) !=
+                HP_OK)
+          return finish(s);
+        if (nd > 0) {
+          const _Float16* in = (j % 2 == 0) ? T0 : T1;
+          _Float16* out = (j % 2 == 0) ? T1 : T0;
+          if ((s = decode_cells(d->gbs, nd, pos.data(), slot.data(), d->h1, d->h2, d->heads,
+                                layers[j], in + dlo * gh, kv[j], out + dlo * gh, ws, L, st,
+                                topk_max_t)) != HP_OK)
+            return finish(s);
+        }
+      }
+      for (int k = dlo; k <= dhi; ++k) {
+        _Float16* dst = (_Float16*)t_out + ((int64_t)(it - k - 1) * d->b) * h1 + k * gh;
+        if ((s = hip_ok(hipMemcpyAsync(dst, last + k * gh, gh * 2, hipMemcpyDeviceToDevice, st),
+                        "hipMemcpyAsync")) != HP_OK)
+          return finish(s);
+      }
+    }
+    return finish(HP_OK);
+  }
+
   // zig-zag ([FlexGen] section 4, Algorithm 1): step 0 is the prefill column;
   // within a step, layer j runs for every GPU batch before layer j + 1.  The
   // GPU batches of a layer share one launch (weights read once per step)
@@ -658,7 +745,7 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   const int parts = mb ? nbat : 1, nb = mb ? d->gbs : d->b;
   for (int j = 0; j < d->l; ++j)
     for (int k = 0; k < parts; ++k)
-      if ((s = prefill_layer(j, (int64_t)k * nb, nb)) != HP_OK) return finish(s);
+      if ((s = prefill_layer(j, (int64_t)k * nb, nb, (int64_t)k * nb)) != HP_OK) return finish(s);
   if (times_ms) hipEventRecord(ev[1], st);
   if (d->n == 0) return finish(HP_OK);
 

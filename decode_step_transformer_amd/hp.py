@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhp.so")
 
 HP_F16, HP_Q4 = 0, 1
-HP_GRAPH, HP_ROW_BY_ROW, HP_MICROBATCH, HP_TOPK10 = 1, 2, 4, 8
+HP_GRAPH, HP_ROW_BY_ROW, HP_MICROBATCH, HP_TOPK10, HP_DIAGONAL = 1, 2, 4, 8, 16
 
 
 class HPError(RuntimeError):

@@ -262,9 +262,18 @@ enum {
   HP_ROW_BY_ROW = 2, /* row-by-row order: each GPU batch runs all steps alone */
   HP_MICROBATCH = 4, /* zig-zag with one launch per GPU batch (gbs rows)
                         instead of one launch per block */
-  HP_TOPK10 = 8      /* decode columns use Top-K sparse attention keeping
+  HP_TOPK10 = 8,     /* decode columns use Top-K sparse attention keeping
                         ceil(T / 10) of the T visible rows ([FlexGen] section 5,
                         sparse attention; see hp_topk_attention); s + n <= 4096 */
+  HP_DIAGONAL = 16   /* diagonal block schedule ([FlexGen] appendix A.2, Fig. 5):
+                        GPU batch k runs step it - k of iteration it (0 = its
+                        prefill), layer-major over the batches of each
+                        iteration; results equal the zig-zag block's.  Batch k
+                        keeps its cache in slot k mod min(b / gbs, n + 1), so
+                        kv[j] needs only that many GPU batches of requests.
+                        Eager launches: not with HP_GRAPH, HP_ROW_BY_ROW or
+                        HP_MICROBATCH (HP_ERR_SHAPE).  times_ms[0] = 0,
+                        times_ms[1] = the whole schedule */
 };
 
 /* [FlexGen] section 4, Algorithm 1: zig-zag block schedule over one block of

@@ -152,3 +152,79 @@ def test_graph_replays_repeat(hp, orc):
     a = _run_gpu_block(hp, c, layers, x, t, c["b"], hp.HP_GRAPH)
     b_ = _run_gpu_block(hp, c, layers, x, t, c["b"], hp.HP_GRAPH)
     assert np.array_equal(a[1].view(np.uint16), b_[1].view(np.uint16))
+
+
+def _run_block_slots(hp, c, layers, x, t, gbs, flags, nreq):
+    """The block with caches for nreq requests (the diagonal schedule's slot ring)."""
+    import torch
+    b, s, n, h1, heads = c["b"], c["s"], c["n"], c["h1"], c["heads"]
+    d = hp.dims(b, s, n, h1, c["h2"], c["l"], heads, gbs)
+    ws = torch.empty(hp.hp_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    kvs = [hp.KVCache(1, nreq, heads, s + n, h1 // heads) for _ in layers]
+    xo = torch.empty((b, s, h1), dtype=torch.float16, device="cuda")
+    to = torch.empty((n, b, h1), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        hp.hp_run_block(d, layers, dev(x), dev(t), kvs, xo, to, ws, flags, stream=stream)
+    stream.synchronize()
+    return host(xo), host(to), [(host(k.k), host(k.v), host(k.k_sm)) for k in kvs]
+
+
+@pytest.mark.parametrize("b,gbs,n", [(4, 1, 8), (4, 2, 8), (6, 1, 3), (8, 2, 2)])
+def test_diagonal_schedule_equals_zigzag(hp, orc, b, gbs, n):
+    """[FlexGen] appendix A.2: the diagonal block schedule gives the zig-zag
+    block's outputs bit for bit, and the caches of the batches that end in
+    each slot; with more GPU batches than n + 1 the cache slots are reused.
+    The zig-zag reference launches its prefill per GPU batch (HP_MICROBATCH),
+    as the diagonal does: a whole-block prefill of more than 144 rows takes the
+    tiled GEMM kernel, whose sums are ordered differently."""
+    c0 = CONFIGS[1]
+    c = dict(c0, b=b, n=n)
+    l, h1, h2, s = c["l"], c["h1"], c["h2"], c["s"]
+    Ws = [layer_weights(1, j, h1, h2) for j in range(l)]
+    layers = [_gpu_layer(hp, W, 1) for W in Ws]
+    x = synth.normal_f16(synth.seed_for(1), 6000 + b, (b, s, h1))
+    t = synth.normal_f16(synth.seed_for(1), 6001 + b, (n, b, h1))
+    nb = b // gbs
+    nslot = min(nb, n + 1)
+    zx, zt, zk = _run_block_slots(hp, c, layers, x, t, gbs, hp.HP_GRAPH | hp.HP_MICROBATCH, b)
+    dx, dt, dk = _run_block_slots(hp, c, layers, x, t, gbs, hp.HP_DIAGONAL, nslot * gbs)
+    assert np.array_equal(dx.view(np.uint16), zx.view(np.uint16))
+    assert np.array_equal(dt.view(np.uint16), zt.view(np.uint16))
+    for j in range(l):
+        for sl in range(nslot):  # the last batch that used slot sl
+            k = max(kk for kk in range(nb) if kk % nslot == sl)
+            for a, z in zip(dk[j], zk[j]):
+                assert np.array_equal(a[sl * gbs:(sl + 1) * gbs], z[k * gbs:(k + 1) * gbs])
+    if nb > n + 1:  # slot reuse: also against the oracle's diagonal order
+        Wo = [oracle_weights(orc, W, 1) for W in Ws]
+        kref = [orc.KV(1, nslot * gbs, c["heads"], s + n, h1 // c["heads"]) for _ in Ws]
+        rx, rt = orc.run_block(x, t, Wo, kref, c["heads"], gbs, 2)
+        assert_close(dx, rx, what="diagonal prefill output")
+        assert_close(dt, rt, what="diagonal decode outputs")
+
+
+def test_diagonal_schedule_with_topk(hp):
+    """Top-K attention inside the diagonal schedule equals Top-K attention in
+    the zig-zag block bit for bit (every (request, head) is independent)."""
+    c = dict(CONFIGS[1], b=6, n=3)
+    Ws = [layer_weights(1, j, c["h1"], c["h2"]) for j in range(c["l"])]
+    layers = [_gpu_layer(hp, W, 1) for W in Ws]
+    x = synth.normal_f16(synth.seed_for(1), 6100, (c["b"], c["s"], c["h1"]))
+    t = synth.normal_f16(synth.seed_for(1), 6101, (c["n"], c["b"], c["h1"]))
+    _, zt, _ = _run_block_slots(hp, c, layers, x, t, 1,
+                                hp.HP_GRAPH | hp.HP_MICROBATCH | hp.HP_TOPK10, c["b"])
+    _, dt, _ = _run_block_slots(hp, c, layers, x, t, 1, hp.HP_DIAGONAL | hp.HP_TOPK10, 4)
+    assert np.array_equal(dt.view(np.uint16), zt.view(np.uint16))
+
+
+def test_diagonal_schedule_rejects_flag_mixes(hp):
+    import torch
+    c = CONFIGS[1]
+    Ws = [layer_weights(1, j, c["h1"], c["h2"]) for j in range(c["l"])]
+    layers = [_gpu_layer(hp, W, 1) for W in Ws]
+    x = prompt(1, c["b"], c["s"], c["h1"])
+    t = decode_inputs(1, c["n"], c["b"], c["h1"])
+    for extra in (hp.HP_GRAPH, hp.HP_ROW_BY_ROW, hp.HP_MICROBATCH):
+        with pytest.raises(hp.HPError):
+            _run_block_slots(hp, c, layers, x, t, 2, hp.HP_DIAGONAL | extra, c["b"])
