@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
 // the tree visibility: every prefix row, plus tree rows flagged in the
 // query's mask (or rows up to the query's own for a chain).
 template <int D>
-__global__ __launch_bounds__(256) void k_multi_attn(DecArgs a) {
+__global__ __launch_bounds__(256, 2) void k_multi_attn(DecArgs a) {
   constexpr int KS = D / 32, DB = D / 16, RB = 2 * D, SPR = RB / 16;
   constexpr int CB = D / 2;           // code bytes per cache row
   constexpr int NG = D / 64;          // groups per row

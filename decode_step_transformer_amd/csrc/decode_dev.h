@@ -24,17 +24,6 @@
 namespace hp {
 
 // ------------------------------------------------------------ reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
 __device__ __forceinline__ f16x2 h2_of(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
 // Cross-lane moves on the DPP path (no LDS round trip).
