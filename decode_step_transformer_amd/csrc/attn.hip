@@ -325,8 +325,20 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int s = a.s;
   const int nqb = (s + PF_QB - 1) / PF_QB;
-  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);  // longest query blocks first
-  const int rh = blockIdx.x / nqb;
+  // Workgroup ids go to the 8 XCDs round-robin (id % 8), each XCD with its
+  // own L2: the query blocks of one (request, head) run in consecutive turns
+  // of one XCD, so their common K/V prefix is fetched from HBM once there.
+  const int nrh = (int)gridDim.x / nqb, full = (nrh / 8) * 8 * nqb, id = blockIdx.x;
+  int rh, jq;
+  if (id < full) {
+    const int t = id / 8;
+    rh = 8 * (t / nqb) + id % 8;
+    jq = t % nqb;
+  } else {
+    rh = (nrh / 8) * 8 + (id - full) / nqb;
+    jq = (id - full) % nqb;
+  }
+  const int qb = nqb - 1 - jq;  // longest query blocks first
   const int h = rh % a.H, r = rh / a.H;
   const int64_t ld = 3LL * a.h1;
   const _Float16* base = a.qkv + (int64_t)r * s * ld + h * D;

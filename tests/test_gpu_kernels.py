@@ -196,13 +196,16 @@ def test_decode_attention(hp, orc, fmt, D, P, q, tree):
     assert_close(host(out), ref, what="decode attention")
 
 
+@pytest.mark.parametrize("b", [2, 5])
 @pytest.mark.parametrize("D,s", [(64, 1), (64, 37), (128, 64), (128, 150)])
-def test_prefill_attention(hp, orc, D, s):
-    b, heads = 2, 3
+def test_prefill_attention(hp, orc, D, s, b):
+    """b = 5 gives 15 or 20 (request, head) pairs: whole groups of 8 pairs share
+    an XCD's L2 turn by turn, the remainder runs in plain order."""
+    heads = 3
     h1 = heads * D
     if h1 % 128:
         heads, h1 = 4, 4 * D
-    qkv = synth.normal_f16(SEED, 80 + s, (b, s, 3 * h1))
+    qkv = synth.normal_f16(SEED, 80 + s + b, (b, s, 3 * h1))
     out = hp.hp_prefill_attention(b, s, h1, heads, dev(qkv))
     ref = np.zeros((b, s, h1), np.float16)
     for r in range(b):
