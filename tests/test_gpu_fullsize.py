@@ -134,8 +134,8 @@ def test_fullsize_layer(hp, orc, cid, kind):
     _check_cache(orc, kv, rows, kref, T, T + 1, False, f"config {cid} new cache row")
 
 
-def test_fullsize_tree_attention(hp, orc):
-    """b = 8 requests, 2048-row int4 prefix, 64 tree tokens with random BFS parents."""
+def _tree_case(hp, orc):
+    """The tree workload's cache and tree tokens on both sides (codes checked equal)."""
     import torch
     c = CONFIGS[5]
     b, h1, heads, P, q = c["b"], c["h1"], c["heads"], c["prefix"], c["q"]
@@ -163,6 +163,15 @@ def test_fullsize_tree_attention(hp, orc):
     orc.kv_append(kref, kp, vp, 0)
     orc.kv_append(kref, qkv_t[:, :, h1:2 * h1], qkv_t[:, :, 2 * h1:], P)
     _check_cache(orc, kv, rows, kref, 0, P + q, True, "tree cache")
+    return c, kv, kref, qkv_t, qt, parents, masks, mref, out
+
+
+def test_fullsize_tree_attention(hp, orc):
+    """b = 8 requests, 2048-row int4 prefix, 64 tree tokens with random BFS parents."""
+    c, kv, kref, qkv_t, qt, parents, masks, mref, out = _tree_case(hp, orc)
+    b, h1, heads, P, q = c["b"], c["h1"], c["heads"], c["prefix"], c["q"]
+    D = h1 // heads
+    rows = range(b)
     K, V = kref.values("k", P + q), kref.values("v", P + q)
     ref = np.zeros((b, q, h1), np.float16)
 
@@ -174,3 +183,40 @@ def test_fullsize_tree_attention(hp, orc):
     with cf.ThreadPoolExecutor(16) as ex:
         list(ex.map(one, [(r, h) for r in rows for h in range(heads)]))
     assert_close(out, ref, what="tree attention")
+
+
+def test_fullsize_tree_pruning(hp, orc):
+    """The tree workload after verification ([SpecPipe] 2.2.1 sub-tree pruning,
+    2.2.2): one verified token per request; plans and the whole compacted int4
+    cache (all 64 heads) bit-exact against the oracle; attention of the kept
+    tokens over the compacted cache with the new masks on sampled heads."""
+    c, kv, kref, qkv_t, qt, parents, masks, mref, out = _tree_case(hp, orc)
+    b, h1, heads, P, q = c["b"], c["h1"], c["heads"], c["prefix"], c["q"]
+    D = h1 // heads
+    seed = synth.seed_for(5)
+    verified = (synth.words(seed, 7000, 0, b) % np.uint64(q)).astype(np.int32)
+    new_parent, src, kept, err = hp.hp_tree_prune(dev(parents.astype(np.int32)), dev(verified))
+    assert int(host(err)[0]) == 0
+    npar, srch, kepth = host(new_parent), host(src), host(kept)
+    for r in range(b):
+        rp, rs, rk = orc.tree_prune(parents[r], int(verified[r]))
+        assert int(kepth[r]) == rk and np.array_equal(npar[r], rp) and np.array_equal(srch[r], rs)
+    hp.hp_kv_compact(b, q, h1, heads, P, src, kept, kv)
+    orc.kv_compact(kref, P, srch, kepth)
+    for name, oname in (("k", "k"), ("v", "v"), ("k_sm", "ksm"), ("v_sm", "vsm")):
+        assert np.array_equal(host(getattr(kv, name)), getattr(kref, oname)), name
+    new_masks, e2 = hp.hp_tree_masks(new_parent)
+    assert int(host(e2)[0]) == 0
+    q2 = np.zeros_like(qkv_t)
+    for r in range(b):
+        q2[r, :kepth[r]] = qkv_t[r, srch[r, :kepth[r]]]
+    out2 = host(hp.hp_decode_attention(b, q, h1, heads, dev(q2), P, kv, masks=new_masks))
+    K, V = kref.values("k", P + q), kref.values("v", P + q)
+    for r, h in ((0, 0), (1, 17), (2, 33), (3, 63), (4, 5), (5, 40), (6, 21), (7, 58)):
+        k = int(kepth[r])
+        sl = slice(h * D, (h + 1) * D)
+        m = orc.tree_masks(npar[r])[:k]
+        ref = orc.attention(q2[r, :k, sl], K[r, h], V[r, h], [P] * k, m, P)
+        assert_close(out2[r, :k, sl], ref, what=f"pruned tree attention r{r} h{h}")
+        # the kept tokens' outputs equal their outputs before pruning, within rounding
+        assert_close(out2[r, :k, sl], out[r, srch[r, :k], sl], what=f"before/after r{r} h{h}")
