@@ -12,7 +12,10 @@
 //  * The activation tile x[BM][128] of each k-block is staged through LDS
 //    (three stages, rows padded by 16 B) and shared by the 8 waves.
 //  * Weight fragments (fp16, wt[n][k] rows) go straight from HBM to
-//    registers, four 16-byte chunks per lane and subtile per k-block.
+//    registers, four 16-byte chunks per lane and subtile per k-block.  The
+//    k-steps keep the operand layout's natural order (k-step j of a block is
+//    k = 32 j .. 32 j + 31, lane quarter q holding 32 j + 8 q .. + 7), so
+//    each load instruction reads 64 contiguous bytes from each of 16 rows.
 //  * MFMA operand A is the weight fragment (16 output columns), operand B the
 //    activation fragment (16 rows), so each lane ends with 4 consecutive
 //    output columns of one row: 8-byte stores.
@@ -125,12 +128,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int 
   struct Raw {
     u32x4 c[4];  // the 4 k-steps of one k-block
   };
-  const _Float16* Bh = g.B + (int64_t)(n_ld + r16) * g.K + 32 * kq;
+  const _Float16* Bh = g.B + (int64_t)(n_ld + r16) * g.K + 8 * kq;
   auto load_b = [&](Raw& R, int kb) __attribute__((always_inline)) {
     const u32x4* p = (const u32x4*)(Bh + (int64_t)kb * BK);
     unroll<4>([&](auto j_) {
       constexpr int j = decltype(j_)::value;
-      R.c[j] = p[j];
+      R.c[j] = p[4 * j];
     });
   };
 
@@ -140,7 +143,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int 
   // ---- one MFMA k-step (32 deep): fragments of (stage, j) ----
   f16x8 xa[TM], xb[TM], wa, wb;
   auto read_x = [&](f16x8 (&x)[TM], int stage, int j) __attribute__((always_inline)) {
-    const _Float16* Ab = As(stage) + (16 * rt0 + r16) * LDS_ROW + 32 * kq + 8 * j;
+    const _Float16* Ab = As(stage) + (16 * rt0 + r16) * LDS_ROW + 8 * kq + 32 * j;
     unroll<TM>([&](auto i_) {
       constexpr int i = decltype(i_)::value;
       x[i] = *(const f16x8*)(Ab + 16 * i * LDS_ROW);
@@ -167,11 +170,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int 
   // slots 0 and 1 hold kb0 and kb0+1; registers hold block kb0+2
   load_a(kb0);
   load_b(r0, kb0);
-  load_b(r1, clampk(kb0 + 1));
   store_a(0);
   load_a(clampk(kb0 + 1));
   store_a(1);
   load_a(clampk(kb0 + 2));
+  // issued after the last activation load, so that on entry to the loop the
+  // activation registers are followed by one k-block of weight loads, as at
+  // every back edge: the compiler's memory-counter wait at the loop head is
+  // then the steady-state one instead of a wait for the next weights too
+  load_b(r1, clampk(kb0 + 1));
   __syncthreads();
   read_x(xa, 0, 0);
   make_w(wa, r0, std::integral_constant<int, 0>());
@@ -258,10 +265,31 @@ __global__ __launch_bounds__(512, 2) void k_gemm(GemmArgs g) {
   gemm_tile<TM, 512, SR>(g, As, threadIdx.x, wave, 0, (int64_t)mt * 16 * TM, nt);
 }
 
-// Sums split-k partials in split order, then applies the epilogue.
-__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ P, int splits,
-                                                       int64_t M, int N,
-                                                       const _Float16* __restrict__ res,
+// Calls f(std::integral_constant<int, n>()) for a split count n in [2, 16]
+// (the range split_for produces) and returns true; false otherwise.
+template <int N = 2, class F>
+static bool with_split_count(int n, F&& f) {
+  if constexpr (N > 16) {
+    (void)n;
+    (void)f;
+    return false;
+  } else {
+    if (n == N) {
+      f(std::integral_constant<int, N>());
+      return true;
+    }
+    return with_split_count<N + 1>(n, f);
+  }
+}
+
+// Sums split-k partials in split order, then applies the epilogue.  The
+// split count is a template argument so that a thread issues the loads of
+// all S splits before the first add (with a run-time count each load waited
+// for the previous add; the partials of an M = 64 product are a few MB, so
+// the sum is bound by that latency); the adds still go in split order.
+template <int S>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ P, int64_t M,
+                                                       int N, const _Float16* __restrict__ res,
                                                        int64_t ldr, int relu,
                                                        _Float16* __restrict__ Y, int64_t ldy) {
   const int64_t quads = M * (N / 4);
@@ -269,14 +297,19 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += stride) {
     const int64_t m = q / (N / 4);
     const int n = (int)(q % (N / 4)) * 4;
-    f32x4 v = *(const f32x4*)(P + m * N + n);
-    for (int s = 1; s < splits; ++s) v += *(const f32x4*)(P + ((int64_t)s * M + m) * N + n);
+    f32x4 p[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) p[s] = *(const f32x4*)(P + ((int64_t)s * M + m) * N + n);
+    f16x4 r = {};
+    if (res) r = *(const f16x4*)(res + m * ldr + n);
+    f32x4 v = p[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) v += p[s];
     if (relu) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
     }
     if (res) {
-      const f16x4 r = *(const f16x4*)(res + m * ldr + n);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] += (float)r[e];
     }
@@ -380,8 +413,12 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
     const int64_t quads = M * (w.n / 4);
     const int blocks = (int)std::min<int64_t>(cdiv(quads, 256), 8192);
     Prof prof("gemm_splitk_reduce", st);
-    hipLaunchKernelGGL(k_splitk_reduce, dim3(blocks), dim3(256), 0, st, (const float*)ws, splits,
-                       M, w.n, (const _Float16*)res, ldr, relu ? 1 : 0, (_Float16*)y, ldy);
+    const bool known = with_split_count(splits, [&](auto s_) {
+      hipLaunchKernelGGL(k_splitk_reduce<decltype(s_)::value>, dim3(blocks), dim3(256), 0, st,
+                         (const float*)ws, M, w.n, (const _Float16*)res, ldr, relu ? 1 : 0,
+                         (_Float16*)y, ldy);
+    });
+    if (!known) return fail(HP_ERR_SHAPE, "k_splitk_reduce: split count out of range");
     return launch_ok("k_splitk_reduce");
   }
   // tall products: fp16 MFMA kernel over LDS tiles; int4 weights are first
