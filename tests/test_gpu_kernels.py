@@ -108,6 +108,22 @@ def test_gemm(hp, orc, fmt, M, K, N, epi):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("KB", range(5, 17))
+def test_gemm_split_counts(hp, orc, fmt, KB):
+    """Skinny products with one column tile and k = 128 KB: both split rules
+    give KB split-K partial sums (every count the sum kernels are built for
+    beyond those of test_gemm), with the residual epilogue."""
+    M, K, N = 64 if KB % 2 else 144, 128 * KB, 256
+    x = synth.normal_f16(SEED, 60 + KB, (M, K))
+    w = synth.normal_f16(SEED, 61 + KB, (K, N), 0.05)
+    res = synth.normal_f16(SEED, 62 + KB, (M, N))
+    m = hp.make_weight(dev(w), fmt)
+    y = hp.hp_gemm(dev(x), m, res=dev(res))
+    ref = _ref_gemm(orc, x, w, fmt, res, False)
+    assert_close(host(y), ref, what=f"gemm fmt={fmt} K={K}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
 def test_gemm_rows_do_not_depend_on_m(hp, fmt):
     """Skinny products reduce k in an order fixed by (k, n): any row subset of
     a batch of up to 144 rows gives bitwise the same rows."""
