@@ -17,7 +17,8 @@
 //    distinct banks.  The direct loads are issued from inline assembly and
 //    their completion is awaited explicitly (vmcnt) before each barrier.
 //  * Fragments of the next k-step are read from LDS while the MFMAs of the
-//    current one run.
+//    current one run: after each k-step's barrier the MFMAs start at once,
+//    with those reads and the direct loads spread among them.
 #include <type_traits>
 
 #include "common.h"
@@ -118,14 +119,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mma = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[buf][t], fa[buf][i], acc[i][t], 0, 0, 0);
-  };
-
   const int KS = g.K / G_BK;
   auto ck = [&](int ks) __attribute__((always_inline)) { return min(ks, KS - 1); };
   // prologue: k-steps 0..3 in flight, fragments of step 0 in registers
@@ -140,16 +133,46 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
   // step kk: fragments of kk in buffer kk&1; stage (kk+1)&3 must be complete
   // (its loads were issued three steps earlier); stage kk&3 is refilled with
   // step kk+4 once every wave has passed this step's barrier.
+  // After the barrier the MFMAs of step kk start at once; the fragment reads
+  // of step kk+1 and the four direct loads of step kk+4 are spread over the
+  // four groups of 8 MFMAs (two accumulator rows each), so that the matrix
+  // cores are not idle while both waves of a SIMD issue memory instructions.
   auto step = [&](int kk, auto cur_) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_)::value;
     wait_vm<8, 0>();  // this wave's reads of stage kk are done, and its loads of kk+1
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(ck(kk + 4), kk & 3);
-    read(cur ^ 1, (kk + 1) & 3);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(cur);
-    __builtin_amdgcn_sched_barrier(0);
+    const int64_t ko = (int64_t)ck(kk + 4) * G_BK;
+    const uint32_t stg = sbase + (uint32_t)(kk & 3) * G_STAGE * 2;
+    const _Float16* St = S + ((kk + 1) & 3) * G_STAGE;
+    const int slot = (kq ^ ((r16 >> 1) & 3)) * 8;
+    unroll16<4>([&](auto c_) {
+      constexpr int c = decltype(c_)::value;
+      const _Float16* Sa = St + (128 * wm + 32 * c + r16) * 32 + slot;
+      fa[cur ^ 1][2 * c] = *(const f16x8*)Sa;
+      fa[cur ^ 1][2 * c + 1] = *(const f16x8*)(Sa + 16 * 32);
+      fb[cur ^ 1][c] = *(const f16x8*)(St + G_BM * 32 + (64 * wn + 16 * c + r16) * 32 + slot);
+      unroll16<2>([&](auto i_) {
+        constexpr int i = 2 * c + decltype(i_)::value;
+        unroll16<4>([&](auto t_) {
+          constexpr int t = decltype(t_)::value;
+          acc[i][t] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[cur][t], fa[cur][i], acc[i][t], 0, 0, 0);
+        });
+      });
+      unroll16<3>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (c < 2)
+        dma16(srcA[c] + ko, __builtin_amdgcn_readfirstlane(stg + (2 * wave + c) * 1024));
+      else
+        dma16(srcB[c - 2] + ko,
+              __builtin_amdgcn_readfirstlane(stg + G_BM * 64 + (2 * wave + c - 2) * 1024));
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   int kk = 0;
   for (; kk + 2 <= KS; kk += 2) {
