@@ -220,3 +220,50 @@ def test_fullsize_tree_pruning(hp, orc):
         assert_close(out2[r, :k, sl], ref, what=f"pruned tree attention r{r} h{h}")
         # the kept tokens' outputs equal their outputs before pruning, within rounding
         assert_close(out2[r, :k, sl], out[r, srch[r, :k], sl], what=f"before/after r{r} h{h}")
+
+
+def test_fullsize_diagonal_schedule(hp):
+    """[FlexGen] appendix A.2 at the OPT-30B int4 block shape (b = 144 in three
+    GPU batches of 48, s = 512, n = 32: the per-layer launches bench.py times
+    under HP_DIAGONAL; two layers): the diagonal schedule gives the outputs and
+    the caches of the zig-zag block that launches its prefill per GPU batch,
+    bit for bit.  Weights and inputs are seeded device draws (no oracle: the
+    claim is equality of two schedules of the same kernels)."""
+    import torch
+    c = CONFIGS[3]
+    l, h1, h2, heads, b, gbs, s, n = 2, c["h1"], c["h2"], c["heads"], c["b"], c["gbs"], c["s"], c["n"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.seed_for(3) & 0x7FFFFFFF)
+    shp = {"wq": (h1, h1), "wk": (h1, h1), "wv": (h1, h1), "wo": (h1, h1), "w1": (h1, h2),
+           "w2": (h2, h1)}
+    layers = []
+    for _ in range(l):
+        W = {k: (torch.randn(v, generator=g, device="cuda") * 0.02).half() for k, v in shp.items()}
+        layers.append(hp.make_layer(W, 1))
+        del W
+    x = torch.randn((b, s, h1), generator=g, device="cuda").half()
+    t = torch.randn((n, b, h1), generator=g, device="cuda").half()
+    nb = b // gbs
+    nslot = min(nb, n + 1)
+    d = hp.dims(b, s, n, h1, h2, l, heads, gbs)
+    ws = torch.empty(hp.hp_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def run(flags, nreq):
+        kvs = [hp.KVCache(1, nreq, heads, s + n, h1 // heads) for _ in range(l)]
+        xo = torch.empty((b, s, h1), dtype=torch.float16, device="cuda")
+        to = torch.empty((n, b, h1), dtype=torch.float16, device="cuda")
+        with torch.cuda.stream(stream):
+            hp.hp_run_block(d, layers, x, t, kvs, xo, to, ws, flags, stream=stream)
+        stream.synchronize()
+        return xo, to, kvs
+
+    zx, zt, zk = run(hp.HP_GRAPH | hp.HP_MICROBATCH, b)
+    dx, dt, dk = run(hp.HP_DIAGONAL, nslot * gbs)
+    assert nslot == nb  # no slot reuse at this shape: slot k holds GPU batch k
+    assert torch.equal(dx.view(torch.int16), zx.view(torch.int16))
+    assert torch.equal(dt.view(torch.int16), zt.view(torch.int16))
+    for a, z in zip(dk, zk):
+        for u, v in ((a.k, z.k), (a.v, z.v), (a.k_sm, z.k_sm), (a.v_sm, z.v_sm)):
+            assert torch.equal(u, v)
+    assert bool(torch.isfinite(zt.float()).all())
