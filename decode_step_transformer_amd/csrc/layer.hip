@@ -313,12 +313,13 @@ Prof::Prof(const char* t, hipStream_t s) : tag(t), st(s) {
   std::lock_guard<std::mutex> lk(g_pmu);
   a = pool_event();
   b = pool_event();
-  if (a && b) hipEventRecord(a, st);
+  // best effort: a failed record only loses this sample
+  if (a && b) (void)hipEventRecord(a, st);
 }
 
 Prof::~Prof() {
   if (!a || !b) return;
-  hipEventRecord(b, st);
+  (void)hipEventRecord(b, st);
   std::lock_guard<std::mutex> lk(g_pmu);
   g_prec.push_back({tag, {a, b}});
 }
@@ -654,20 +655,21 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   if (times_ms) {
     for (auto& e : ev)
       if ((s = hip_ok(hipEventCreate(&e), "hipEventCreate")) != HP_OK) return s;
-    hipEventRecord(ev[0], st);
+    if ((s = hip_ok(hipEventRecord(ev[0], st), "hipEventRecord")) != HP_OK) {
+      for (auto& e : ev) (void)hipEventDestroy(e);
+      return s;
+    }
   }
   auto finish = [&](hp_status r) {
     if (times_ms) {
-      if (r == HP_OK) {
-        hipEventRecord(ev[2], st);
-        r = hip_ok(hipEventSynchronize(ev[2]), "hipEventSynchronize");
-        if (r == HP_OK) {
-          hipEventElapsedTime(&times_ms[0], ev[0], ev[1]);
-          hipEventElapsedTime(&times_ms[1], ev[1], ev[2]);
-        }
-      }
+      if (r == HP_OK) r = hip_ok(hipEventRecord(ev[2], st), "hipEventRecord");
+      if (r == HP_OK) r = hip_ok(hipEventSynchronize(ev[2]), "hipEventSynchronize");
+      if (r == HP_OK)
+        r = hip_ok(hipEventElapsedTime(&times_ms[0], ev[0], ev[1]), "hipEventElapsedTime");
+      if (r == HP_OK)
+        r = hip_ok(hipEventElapsedTime(&times_ms[1], ev[1], ev[2]), "hipEventElapsedTime");
       for (auto& e : ev)
-        if (e) hipEventDestroy(e);
+        if (e) (void)hipEventDestroy(e);
     }
     return r;
   };
@@ -675,7 +677,8 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   if (rbr) {
     // row-by-row ([FlexGen] section 4, computation schedule): each GPU batch
     // runs its prefill and all its decode steps before the next batch starts
-    if (times_ms) hipEventRecord(ev[1], st);
+    if (times_ms && (s = hip_ok(hipEventRecord(ev[1], st), "hipEventRecord")) != HP_OK)
+      return finish(s);
     for (int k = 0; k < nbat; ++k) {
       const int64_t r0 = (int64_t)k * d->gbs;
       for (int j = 0; j < d->l; ++j)
@@ -698,7 +701,8 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
     // and so on.  Batch k keeps its cache in slot k mod min(nb, n + 1) from its
     // prefill to its last step.  Prefill and decode interleave: times_ms[0]
     // is 0 and times_ms[1] the whole schedule.
-    if (times_ms) hipEventRecord(ev[1], st);
+    if (times_ms && (s = hip_ok(hipEventRecord(ev[1], st), "hipEventRecord")) != HP_OK)
+      return finish(s);
     const int nslot = std::min(nbat, d->n + 1);
     std::vector<int> pos((size_t)nbat), slot((size_t)nbat);
     const int64_t gh = (int64_t)d->gbs * h1;
@@ -746,7 +750,8 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   for (int j = 0; j < d->l; ++j)
     for (int k = 0; k < parts; ++k)
       if ((s = prefill_layer(j, (int64_t)k * nb, nb, (int64_t)k * nb)) != HP_OK) return finish(s);
-  if (times_ms) hipEventRecord(ev[1], st);
+  if (times_ms && (s = hip_ok(hipEventRecord(ev[1], st), "hipEventRecord")) != HP_OK)
+    return finish(s);
   if (d->n == 0) return finish(HP_OK);
 
   launch_set_i32(dstep, 0, false, st);
@@ -779,12 +784,12 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
     hipGraph_t g = nullptr;
     const hipError_t e = hipStreamEndCapture(st, &g);
     if (body != HP_OK) {
-      if (g) hipGraphDestroy(g);
+      if (g) (void)hipGraphDestroy(g);
       return finish(body);
     }
     if ((s = hip_ok(e, "hipStreamEndCapture")) != HP_OK) return finish(s);
     const hipError_t ei = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
-    hipGraphDestroy(g);
+    (void)hipGraphDestroy(g);
     if ((s = hip_ok(ei, "hipGraphInstantiate")) != HP_OK) return finish(s);
     std::lock_guard<std::mutex> lk(g_mu);
     g_graphs[key] = exec;
@@ -814,7 +819,8 @@ int32_t hp_profile_read(char* buf, size_t len) {
     hipError_t e = hipEventSynchronize(r.second.second);
     if (e != hipSuccess) return hip_ok(e, "hipEventSynchronize");
     float ms = 0.f;
-    hipEventElapsedTime(&ms, r.second.first, r.second.second);
+    e = hipEventElapsedTime(&ms, r.second.first, r.second.second);
+    if (e != hipSuccess) return hip_ok(e, "hipEventElapsedTime");
     auto& a = agg[r.first];
     a.first += 1;
     a.second += ms;
@@ -835,7 +841,7 @@ int32_t hp_profile_read(char* buf, size_t len) {
 
 void hp_release_graphs(void) {
   std::lock_guard<std::mutex> lk(g_mu);
-  for (auto& kv : g_graphs) hipGraphExecDestroy(kv.second);
+  for (auto& kv : g_graphs) (void)hipGraphExecDestroy(kv.second);
   g_graphs.clear();
 }
 
