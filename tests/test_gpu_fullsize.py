@@ -253,6 +253,9 @@ def test_fullsize_diagonal_schedule(hp):
         kvs = [hp.KVCache(1, nreq, heads, s + n, h1 // heads) for _ in range(l)]
         xo = torch.empty((b, s, h1), dtype=torch.float16, device="cuda")
         to = torch.empty((n, b, h1), dtype=torch.float16, device="cuda")
+        # the inputs and the zeroed caches come from kernels on the default
+        # stream; the block runs on `stream`, which does not wait for them
+        torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             hp.hp_run_block(d, layers, x, t, kvs, xo, to, ws, flags, stream=stream)
         stream.synchronize()
