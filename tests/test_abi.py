@@ -57,3 +57,21 @@ def test_argument_errors_before_device():
     assert hp.hp_workspace_bytes(d) == 0
     d = hp.dims(4, 32, 8, 256, 1024, 2, 4)
     assert hp.hp_workspace_bytes(d) > 0
+
+
+def test_gemm_host_checks():
+    """hp_gemm on the host: a product with no rows is a no-op that touches no
+    memory (the pointers below are never dereferenced), negative M and bad
+    weight shapes are rejected, all before any device call."""
+    import ctypes as C
+    from decode_step_transformer_amd import hp
+    L = hp.lib()
+    fake = 0x100000  # aligned, never dereferenced
+    m = hp.hp_mat(hp.HP_Q4, 256, 512, fake, fake, fake)
+    assert L.hp_gemm(None, 256, C.byref(m), 0, None, 0, 0, None, 512, None, 0, None) == 0
+    assert L.hp_gemm(None, 256, C.byref(m), -1, None, 0, 0, None, 512, None, 0, None) == -2
+    bad = hp.hp_mat(hp.HP_Q4, 200, 512, fake, fake, fake)               # k % 128 != 0
+    assert L.hp_gemm(None, 200, C.byref(bad), 4, None, 0, 0, None, 512, None, 0, None) == -2
+    nul = hp.hp_mat(hp.HP_Q4, 256, 512, fake, None, fake)               # no scales
+    assert L.hp_gemm(None, 256, C.byref(nul), 4, None, 0, 0, None, 512, None, 0, None) == -1
+    assert L.hp_gemm(None, 256, None, 4, None, 0, 0, None, 512, None, 0, None) == -1
