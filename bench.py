@@ -269,16 +269,16 @@ def tree_prune_step(hp, torch, stream, g, parent, kv, reps):
     b, h1, H, P, q = t["b"], t["h1"], t["heads"], t["prefix"], t["q"]
     D = h1 // H
     verified = torch.randint(0, q, (b,), generator=g, device="cuda", dtype=torch.int32)
-    new_parent, src, kept, err = hp.hp_tree_prune(parent, verified, stream=stream)
-    hp.hp_kv_compact(b, q, h1, H, P, src, kept, kv, stream=stream)
+    new_parent, src, prefix, kept, err = hp.hp_tree_prune(parent, verified, P, stream=stream)
+    hp.hp_kv_compact(b, q, h1, H, P, src, prefix, kept, kv, stream=stream)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     held = hold_stream(torch, stream)
     ev[0].record(stream)
     for _ in range(reps):
-        hp.hp_tree_prune(parent, verified, stream=stream)
+        hp.hp_tree_prune(parent, verified, P, stream=stream)
     ev[1].record(stream)
     for _ in range(reps):  # the same plan each time: the same rows move
-        hp.hp_kv_compact(b, q, h1, H, P, src, kept, kv, stream=stream)
+        hp.hp_kv_compact(b, q, h1, H, P, src, prefix, kept, kv, stream=stream)
     ev[2].record(stream)
     queued_ahead = not held.query()
     stream.synchronize()
@@ -286,12 +286,15 @@ def tree_prune_step(hp, torch, stream, g, parent, kv, reps):
     plan_ms = ev[0].elapsed_time(ev[1]) / reps
     move_ms = ev[1].elapsed_time(ev[2]) / reps
     ks = kept.cpu().tolist()
-    moved = 2.0 * H * sum(ks) * (D / 2 + 4 * D / 64) * 2  # each kept K/V row read and written
+    committed = (prefix.cpu() - P).tolist()
+    moved_rows = sum(ks) + sum(committed)
+    moved = 2.0 * H * moved_rows * (D / 2 + 4 * D / 64) * 2  # each K/V row read and written
     return {"plan_us": plan_ms * 1e3, "compact_us": move_ms * 1e3, "kept": ks,
+            "committed": committed,
             "queued_ahead": queued_ahead,
             "compact_gbs": moved / (move_ms / 1e3) / 1e9,
-            "work": "kept rows x heads x (K, V) x (d/2 + 4*d/64) bytes, read and written once; "
-                    "launch-bound at this size"}
+            "work": "(committed + kept) rows x heads x (K, V) x (d/2 + 4*d/64) bytes, read and "
+                    "written once; launch-bound at this size"}
 
 
 def cpu_baseline(c, cname, seconds_hint=20.0):

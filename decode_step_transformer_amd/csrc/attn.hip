@@ -72,6 +72,7 @@ struct DecArgs {
   const _Float16* qkv;
   int q, h1, H, pos;
   const int32_t* dpos;
+  const int32_t* plen;  // per-request prefix lengths (clamped to [0, pos]), or NULL
   const uint64_t* masks;
   int cap;
   const void* k;
@@ -80,6 +81,13 @@ struct DecArgs {
   const uint32_t* vsm;
   _Float16* out;
 };
+// Cache rows before the new tokens of request r: the same for every request
+// (pos, plus the step counter of a replayed graph), or per request.
+__device__ __forceinline__ int prefix_len(const DecArgs& a, int r) {
+  if (a.plen) return min(max(a.plen[r], 0), a.pos);
+  return a.pos + (a.dpos ? *a.dpos : 0);
+}
+
 template <int D, bool Q4, bool MASKED>
 __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   using S = DecShape<D, Q4>;
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   const int i = blockIdx.x % a.q;
   const int rh = blockIdx.x / a.q;
   const int h = rh % a.H, r = rh / a.H;
-  const int P = a.pos + (a.dpos ? *a.dpos : 0);
+  const int P = prefix_len(a, r);
   const int R = MASKED ? P + a.q : P + i + 1;
   const uint64_t mask = MASKED ? a.masks[(int64_t)r * a.q + i] : 0ull;
   // wave-uniform bases, per-lane 32-bit byte offsets
@@ -419,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void k_multi_attn(DecArgs a) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, G = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = blockIdx.x % a.H, r = blockIdx.x / a.H;
-  const int P = a.pos + (a.dpos ? *a.dpos : 0);
+  const int P = prefix_len(a, r);
   const int R = P + a.q;
   const int qi = 16 * wave + r16;
   const int qrow = min(qi, a.q - 1);
@@ -547,10 +555,10 @@ void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const voi
 }
 
 void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
-                             int32_t pos, const int32_t* dpos, const uint64_t* masks,
-                             const hp_kv& kv, void* out, hipStream_t st) {
-  DecArgs a{(const _Float16*)qkv, q,     h1,   heads, pos,  dpos,
-            masks,                kv.cap, kv.k, kv.v,  (const uint32_t*)kv.k_sm,
+                             int32_t pos, const int32_t* dpos, const int32_t* plen,
+                             const uint64_t* masks, const hp_kv& kv, void* out, hipStream_t st) {
+  DecArgs a{(const _Float16*)qkv, q,      h1,   heads, pos,  dpos,
+            plen,                 masks,  kv.cap, kv.k, kv.v, (const uint32_t*)kv.k_sm,
             (const uint32_t*)kv.v_sm, (_Float16*)out};
   const int D = h1 / heads;
   if (kv.fmt == HP_Q4 && q >= 16) {

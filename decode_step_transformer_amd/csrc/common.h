@@ -85,9 +85,11 @@ void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const voi
                       int32_t pos, const int32_t* dpos, const hp_kv& kv, hipStream_t st);
 void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, const void* qkv,
                               void* out, hipStream_t st);
+// plen (device int32 [b], may be NULL): per-request prefix lengths, each
+// clamped to [0, pos]; then dpos is ignored.
 void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
-                             int32_t pos, const int32_t* dpos, const uint64_t* masks,
-                             const hp_kv& kv, void* out, hipStream_t st);
+                             int32_t pos, const int32_t* dpos, const int32_t* plen,
+                             const uint64_t* masks, const hp_kv& kv, void* out, hipStream_t st);
 // Top-K sparse decode attention (one query per request); visible rows
 // [0, pos + *dpos + 1) with max_t bounding that count (<= 4096); topk = 0
 // keeps ceil(T / 10).  Returns HP_ERR_SHAPE if max_t is out of range.
@@ -96,11 +98,12 @@ hp_status launch_topk_attention(int32_t b, int32_t h1, int32_t heads, const void
                                 void* out, int32_t* idx, hipStream_t st);
 void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
                        hipStream_t st);
-void launch_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
-                       int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
-                       hipStream_t st);
+void launch_tree_prune(int32_t b, int32_t q, int32_t pos, const int32_t* parent,
+                       const int32_t* verified, int32_t* new_parent, int32_t* src,
+                       int32_t* prefix, int32_t* kept, int32_t* err, hipStream_t st);
 void launch_kv_compact(int32_t b, int32_t q, int32_t heads, int32_t d, int32_t pos,
-                       const int32_t* src, const int32_t* kept, const hp_kv& kv, hipStream_t st);
+                       const int32_t* src, const int32_t* prefix, const int32_t* kept,
+                       const hp_kv& kv, hipStream_t st);
 
 // Small utility kernels used by the block runner.
 void launch_copy_step(const void* src, int64_t count_elems, int64_t stride_elems,

@@ -231,7 +231,8 @@ static hp_status decode_body(int b, int q, int h1, int h2, int heads, const hp_l
       return fail(r, "topk attention: bad row count");
     if ((r = launch_ok("k_topk_attn")) != HP_OK) return r;
   } else {
-    launch_decode_attention(b, q, h1, heads, qkv, pos, dpos, masks, kv, at<void>(ws, L.a), st);
+    launch_decode_attention(b, q, h1, heads, qkv, pos, dpos, nullptr, masks, kv, at<void>(ws, L.a),
+                            st);
     if ((r = launch_ok("k_decode_attn")) != HP_OK) return r;
   }
   return layer_tail(w, M, h1, h2, t, t_out, ws, L, st);
@@ -282,7 +283,7 @@ static hp_status decode_cells(int gbs, int nbat, const int* pos, const int* slot
         return fail(r, "topk attention: bad row count");
       if ((r = launch_ok("k_topk_attn")) != HP_OK) return r;
     } else {
-      launch_decode_attention(gbs, 1, h1, heads, qc, pos[c], nullptr, nullptr, kc, ac, st);
+      launch_decode_attention(gbs, 1, h1, heads, qc, pos[c], nullptr, nullptr, nullptr, kc, ac, st);
       if ((r = launch_ok("k_decode_attn")) != HP_OK) return r;
     }
   }
@@ -457,7 +458,29 @@ hp_status hp_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, c
   hp_status s = check_kv(kv, pos + q);
   if (s != HP_OK) return s;
   if ((s = device_check()) != HP_OK) return s;
-  launch_decode_attention(b, q, h1, heads, qkv, pos, nullptr, masks, *kv, out, S(stream));
+  launch_decode_attention(b, q, h1, heads, qkv, pos, nullptr, nullptr, masks, *kv, out, S(stream));
+  return launch_ok("k_decode_attn");
+}
+
+hp_status hp_decode_attention_ragged(int32_t b, int32_t q, int32_t h1, int32_t heads,
+                                     const void* qkv, const int32_t* prefix, int32_t max_prefix,
+                                     const uint64_t* masks, const hp_kv* kv, void* out,
+                                     void* stream) {
+  if (b <= 0 || h1 <= 0 || heads <= 0 || h1 % heads || max_prefix < 0)
+    return fail(HP_ERR_SHAPE, "bad sizes");
+  if (q < 1 || q > 64) return fail(HP_ERR_TREE, "q must be in [1, 64]");
+  const int D = h1 / heads;
+  if (D != 64 && D != 128) return fail(HP_ERR_SHAPE, "head dim %d not in {64, 128}", D);
+  if (!qkv || !out || !prefix) return fail(HP_ERR_NULL, "NULL pointer");
+  NEED_ALIGN(qkv, 16);
+  NEED_ALIGN(out, 16);
+  NEED_ALIGN(prefix, 4);
+  if (masks) NEED_ALIGN(masks, 8);
+  hp_status s = check_kv(kv, max_prefix + q);
+  if (s != HP_OK) return s;
+  if ((s = device_check()) != HP_OK) return s;
+  launch_decode_attention(b, q, h1, heads, qkv, max_prefix, nullptr, prefix, masks, *kv, out,
+                          S(stream));
   return launch_ok("k_decode_attn");
 }
 
@@ -492,30 +515,61 @@ hp_status hp_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* m
 }
 
 hp_status hp_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
-                        int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
-                        void* stream) {
-  if (b <= 0) return fail(HP_ERR_SHAPE, "b must be positive");
+                        int32_t pos, int32_t* new_parent, int32_t* src, int32_t* prefix,
+                        int32_t* kept, int32_t* err, void* stream) {
+  if (b <= 0 || pos < 0) return fail(HP_ERR_SHAPE, "b must be positive, pos >= 0");
   if (q < 1 || q > 64) return fail(HP_ERR_TREE, "q must be in [1, 64]");
-  if (!parent || !verified || !new_parent || !src || !kept) return fail(HP_ERR_NULL, "NULL pointer");
+  if (!parent || !verified || !new_parent || !src || !prefix || !kept)
+    return fail(HP_ERR_NULL, "NULL pointer");
   hp_status s = device_check();
   if (s != HP_OK) return s;
-  launch_tree_prune(b, q, parent, verified, new_parent, src, kept, err, S(stream));
+  launch_tree_prune(b, q, pos, parent, verified, new_parent, src, prefix, kept, err, S(stream));
   return launch_ok("k_tree_prune");
 }
 
 hp_status hp_kv_compact(int32_t b, int32_t q, int32_t h1, int32_t heads, int32_t pos,
-                        const int32_t* src, const int32_t* kept, const hp_kv* kv, void* stream) {
+                        const int32_t* src, const int32_t* prefix, const int32_t* kept,
+                        const hp_kv* kv, void* stream) {
   if (b <= 0 || h1 <= 0 || heads <= 0 || h1 % heads || pos < 0)
     return fail(HP_ERR_SHAPE, "bad sizes");
   if (q < 1 || q > 64) return fail(HP_ERR_TREE, "q must be in [1, 64]");
   const int D = h1 / heads;
   if (D != 64 && D != 128) return fail(HP_ERR_SHAPE, "head dim %d not in {64, 128}", D);
-  if (!src || !kept) return fail(HP_ERR_NULL, "NULL pointer");
+  if (!src || !prefix || !kept) return fail(HP_ERR_NULL, "NULL pointer");
   hp_status s = check_kv(kv, pos + q);
   if (s != HP_OK) return s;
   if ((s = device_check()) != HP_OK) return s;
-  launch_kv_compact(b, q, heads, D, pos, src, kept, *kv, S(stream));
+  launch_kv_compact(b, q, heads, D, pos, src, prefix, kept, *kv, S(stream));
   return launch_ok("k_kv_compact");
+}
+
+static thread_local hp_capture g_capture;
+static thread_local bool g_capture_on = false;
+
+hp_status hp_debug_set_capture(const hp_capture* c) {
+  g_capture_on = c != nullptr;
+  if (c) g_capture = *c;
+  return HP_OK;
+}
+
+// Copies a finished layer's stored intermediates out (hp_debug_set_capture).
+static hp_status capture_out(int64_t M, int h1, int h2, void* ws, const Ws& L, hipStream_t st) {
+  if (!g_capture_on) return HP_OK;
+  const hp_capture& c = g_capture;
+  const size_t row1 = (size_t)h1 * 2;
+  struct Part { void* dst; size_t src, bytes, pitch; } parts[4] = {
+      {c.qkv, L.qkv, 3 * row1, 3 * row1},
+      {c.attn, L.a, row1, row1},
+      {c.x_out, L.xo, row1, row1},
+      {c.hidden, L.hid, (size_t)h2 * 2, (size_t)pad_ld(h2) * 2}};
+  for (const Part& p : parts) {
+    if (!p.dst) continue;
+    hp_status s = hip_ok(hipMemcpy2DAsync(p.dst, p.bytes, (const char*)ws + p.src, p.pitch, p.bytes,
+                                          (size_t)M, hipMemcpyDeviceToDevice, st),
+                         "capture copy");
+    if (s != HP_OK) return s;
+  }
+  return HP_OK;
 }
 
 size_t hp_workspace_bytes(const hp_dims* d) {
@@ -536,7 +590,10 @@ hp_status hp_layer_prefill(const hp_dims* d, const hp_layer* w, const void* x, c
   const Ws L = ws_layout(*d);
   if (ws_bytes < L.total) return fail(HP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   if ((s = device_check()) != HP_OK) return s;
-  return prefill_body(d->b, d->s, d->h1, d->h2, d->heads, *w, x, *kv, x_out, ws, L, S(stream));
+  if ((s = prefill_body(d->b, d->s, d->h1, d->h2, d->heads, *w, x, *kv, x_out, ws, L,
+                        S(stream))) != HP_OK)
+    return s;
+  return capture_out((int64_t)d->b * d->s, d->h1, d->h2, ws, L, S(stream));
 }
 
 hp_status hp_layer_decode(const hp_dims* d, const hp_layer* w, const void* t, int32_t pos,
@@ -556,8 +613,10 @@ hp_status hp_layer_decode(const hp_dims* d, const hp_layer* w, const void* t, in
   const Ws L = ws_layout(*d);
   if (ws_bytes < L.total) return fail(HP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   if ((s = device_check()) != HP_OK) return s;
-  return decode_body(d->b, q, d->h1, d->h2, d->heads, *w, t, pos, nullptr, masks, *kv, t_out, ws,
-                     L, S(stream));
+  if ((s = decode_body(d->b, q, d->h1, d->h2, d->heads, *w, t, pos, nullptr, masks, *kv, t_out, ws,
+                       L, S(stream))) != HP_OK)
+    return s;
+  return capture_out((int64_t)d->b * q, d->h1, d->h2, ws, L, S(stream));
 }
 
 static void graph_key(std::vector<uint64_t>& key, const hp_dims* d, const hp_layer* layers,

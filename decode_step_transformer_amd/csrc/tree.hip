@@ -68,20 +68,24 @@ __global__ __launch_bounds__(1024) void k_tree_masks(int b, int q, const int32_t
 
 // ------------------------------------------------------------ tree pruning
 // [SpecPipe] 2.2.1 sub-tree pruning (Fig. 5-b) and 2.2.2 (Fig. 8): once
-// token u of a request is verified, the request keeps the tokens on u's path
-// to the root (the verified path, whose cache rows every kept token sees) and
-// u's subtree (the tokens with u as an ancestor), in BFS order.  One wave per
-// request; lane i holds token i: its ancestor set as in k_tree_masks, a
-// ballot of the kept lanes gives each kept token its new index, and a lane
-// shuffle maps its parent to the parent's new index.  Slots past the kept
-// count become filler leaves (the last kept token's parent, or 0 when one
-// token is kept) so the new array stays a valid BFS parent array.  A request
-// with an invalid parent array or verified index keeps nothing and is
-// counted in err.
-__global__ __launch_bounds__(1024) void k_tree_prune(int b, int q, const int32_t* __restrict__ parent,
+// token u of a request is verified, column u of the mask matrix (u and its
+// descendants) is the new tree, with u as its root; the verified path above
+// u (row u of the mask without u) stays in the cache as committed prefix.
+// One wave per request; lane i holds token i: its ancestor set as in
+// k_tree_masks, u's set broadcast by a shuffle.  The rows that stay in the
+// cache (path, then subtree) are the lanes flagged in either set, in index
+// order: a ballot prefix count gives each its position, and the subtree
+// tokens' positions less the path length are their new indices; a shuffle
+// maps each parent to its new index.  Slots past the new tree are filler
+// leaves (the last kept token's parent, or 0 when u is alone) so the new
+// array stays a valid BFS parent array.  A request with an invalid parent
+// array or verified index keeps nothing and is counted in err.
+__global__ __launch_bounds__(1024) void k_tree_prune(int b, int q, int pos,
+                                                     const int32_t* __restrict__ parent,
                                                      const int32_t* __restrict__ verified,
                                                      int32_t* __restrict__ new_parent,
                                                      int32_t* __restrict__ src,
+                                                     int32_t* __restrict__ prefix_out,
                                                      int32_t* __restrict__ kept_out,
                                                      int32_t* __restrict__ err) {
   __shared__ int bad[16];
@@ -97,6 +101,7 @@ __global__ __launch_bounds__(1024) void k_tree_prune(int b, int q, const int32_t
     if (!good) {
       if (i == 0) {
         kept_out[r] = 0;
+        prefix_out[r] = pos;
         ++nbad;
       }
       if (i < q) {
@@ -107,24 +112,27 @@ __global__ __launch_bounds__(1024) void k_tree_prune(int b, int q, const int32_t
     }
     const uint64_t m = ancestor_set(i, q, p0, true);
     const uint64_t mu = shfl_u64(m, u);
-    const bool keep = i < q && (((mu >> i) & 1ull) || ((m >> u) & 1ull));
-    const uint64_t kb = __ballot(keep);
-    const int newidx = __popcll(kb & ((1ull << i) - 1ull));  // kept lanes below i
-    const int kept = __popcll(kb);
-    const int nidx_of_parent = __shfl(newidx, p0 < 0 ? 0 : p0);
-    const int np = p0 < 0 ? -1 : nidx_of_parent;
-    const int last = 63 - __clzll(kb);  // lane of the last kept token
+    const int depth = __popcll(mu) - 1;                  // u's ancestors
+    const bool in_sub = i < q && ((m >> u) & 1ull);      // u or below it
+    const bool stay = in_sub || (i < q && ((mu >> i) & 1ull));
+    const uint64_t sb = __ballot(stay);
+    const int row = __popcll(sb & ((1ull << i) - 1ull));  // position after the old prefix
+    const int rows = __popcll(sb);
+    const int kept = rows - depth;
+    const int nidx = row - depth;                          // new index (subtree lanes)
+    const int nidx_of_parent = __shfl(nidx, p0 < 0 ? 0 : p0);
+    const int np = (i == u || p0 < 0) ? -1 : nidx_of_parent;
+    const int last = 63 - __clzll(sb);  // lane of the last kept token (in the subtree)
     const int np_last = __shfl(np, last);
     const int fill = kept == 1 ? 0 : np_last;
-    if (keep) {
-      npr[newidx] = np;
-      sr[newidx] = i;
+    if (stay) sr[row] = i;
+    if (i < q && i >= rows) sr[i] = -1;
+    if (in_sub) npr[nidx] = np;
+    if (i < q && i >= kept) npr[i] = fill;
+    if (i == 0) {
+      kept_out[r] = kept;
+      prefix_out[r] = pos + depth;
     }
-    if (i < q && i >= kept) {
-      npr[i] = fill;
-      sr[i] = -1;
-    }
-    if (i == 0) kept_out[r] = kept;
   }
   if (i == 0) bad[w] = nbad;
   __syncthreads();
@@ -135,21 +143,23 @@ __global__ __launch_bounds__(1024) void k_tree_prune(int b, int q, const int32_t
   }
 }
 
-// Moves kept tree rows into place after k_tree_prune: one wave per
-// (request, head, K or V); lane j copies the row of kept token j from cache
-// row pos + src[j] to row pos + j (RB bytes of codes or fp16, SMB bytes of
-// scale/min pairs).  Every lane's store depends on its own load and each
-// load instruction covers the whole wave, so all rows are read before any is
-// overwritten.
+// Moves the rows that stay after k_tree_prune into place: one wave per
+// (request, head, K or V); lane j (j < prefix - pos + kept: the committed
+// path, then the new tree) copies cache row pos + src[j] to row pos + j (RB
+// bytes of codes or fp16, SMB bytes of scale/min pairs).  Every lane's store
+// depends on its own load and each load instruction covers the whole wave,
+// so all rows are read before any is overwritten.
 template <int RB, int SMB>
 __global__ __launch_bounds__(64) void k_kv_compact(int q, int heads, int pos, int cap,
                                                    const int32_t* __restrict__ src,
+                                                   const int32_t* __restrict__ prefix,
                                                    const int32_t* __restrict__ kept, uint8_t* k,
                                                    uint8_t* v, uint8_t* ksm, uint8_t* vsm) {
   const int j = threadIdx.x;
   const int t = blockIdx.x & 1, rh = blockIdx.x >> 1;
   const int h = rh % heads, r = rh / heads;
-  const int n = min(max(kept[r], 0), q);  // any kept / src values stay inside rows [pos, pos + q)
+  // any prefix / kept / src values keep the moves inside rows [pos, pos + q)
+  const int n = min(max(prefix[r] - pos + kept[r], 0), q);
   const int64_t row0 = (int64_t)(r * heads + h) * cap + pos;
   uint8_t* base = (t ? v : k) + row0 * RB;
   uint8_t* sbase = SMB ? (t ? vsm : ksm) + row0 * SMB : nullptr;
@@ -179,19 +189,20 @@ void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* ma
                      masks, err);
 }
 
-void launch_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
-                       int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
-                       hipStream_t st) {
+void launch_tree_prune(int32_t b, int32_t q, int32_t pos, const int32_t* parent,
+                       const int32_t* verified, int32_t* new_parent, int32_t* src,
+                       int32_t* prefix, int32_t* kept, int32_t* err, hipStream_t st) {
   Prof prof("tree_prune", st);
-  hipLaunchKernelGGL(k_tree_prune, dim3(1), dim3(64 * std::min(b, 16)), 0, st, b, q, parent,
-                     verified, new_parent, src, kept, err);
+  hipLaunchKernelGGL(k_tree_prune, dim3(1), dim3(64 * std::min(b, 16)), 0, st, b, q, pos, parent,
+                     verified, new_parent, src, prefix, kept, err);
 }
 
 void launch_kv_compact(int32_t b, int32_t q, int32_t heads, int32_t d, int32_t pos,
-                       const int32_t* src, const int32_t* kept, const hp_kv& kv, hipStream_t st) {
+                       const int32_t* src, const int32_t* prefix, const int32_t* kept,
+                       const hp_kv& kv, hipStream_t st) {
   const dim3 grid((unsigned)(2 * b * heads));
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, q, heads, pos, kv.cap, src, kept,
+    hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, q, heads, pos, kv.cap, src, prefix, kept,
                        (uint8_t*)kv.k, (uint8_t*)kv.v, (uint8_t*)kv.k_sm, (uint8_t*)kv.v_sm);
   };
   Prof prof("kv_compact", st);

@@ -40,6 +40,11 @@ class hp_kv(C.Structure):
                 ("k_sm", C.c_void_p), ("v_sm", C.c_void_p)]
 
 
+class hp_capture(C.Structure):
+    _fields_ = [("qkv", C.c_void_p), ("attn", C.c_void_p), ("x_out", C.c_void_p),
+                ("hidden", C.c_void_p)]
+
+
 class hp_dims(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("b", "s", "n", "h1", "h2", "l", "heads", "gbs")]
 
@@ -47,11 +52,13 @@ class hp_dims(C.Structure):
 EXPORTS = [
     "hp_last_error", "hp_device_check", "hp_quantize_g64", "hp_dequantize_g64",
     "hp_pack_weight_q4", "hp_pack_weight_f16", "hp_gemm_workspace_bytes", "hp_gemm",
-    "hp_kv_append", "hp_prefill_attention", "hp_decode_attention", "hp_topk_attention",
+    "hp_kv_append", "hp_prefill_attention", "hp_decode_attention", "hp_decode_attention_ragged",
+    "hp_topk_attention",
     "hp_tree_masks",
     "hp_tree_prune", "hp_kv_compact",
     "hp_workspace_bytes", "hp_layer_prefill", "hp_layer_decode", "hp_run_block",
     "hp_release_graphs", "hp_weight_bytes", "hp_kv_bytes", "hp_profile", "hp_profile_read",
+    "hp_debug_set_capture",
 ]
 
 _lib = None
@@ -78,8 +85,10 @@ def lib():
             "hp_decode_attention": [_i32, _i32, _i32, _i32, _p, _i32, _p, C.POINTER(hp_kv), _p, _p],
             "hp_topk_attention": [_i32, _i32, _i32, _p, _i32, _i32, C.POINTER(hp_kv), _p, _p, _p],
             "hp_tree_masks": [_i32, _i32, _p, _p, _p, _p],
-            "hp_tree_prune": [_i32, _i32, _p, _p, _p, _p, _p, _p, _p],
-            "hp_kv_compact": [_i32, _i32, _i32, _i32, _i32, _p, _p, C.POINTER(hp_kv), _p],
+            "hp_decode_attention_ragged": [_i32, _i32, _i32, _i32, _p, _p, _i32, _p,
+                                           C.POINTER(hp_kv), _p, _p],
+            "hp_tree_prune": [_i32, _i32, _p, _p, _i32, _p, _p, _p, _p, _p, _p],
+            "hp_kv_compact": [_i32, _i32, _i32, _i32, _i32, _p, _p, _p, C.POINTER(hp_kv), _p],
             "hp_layer_prefill": [C.POINTER(hp_dims), C.POINTER(hp_layer), _p, C.POINTER(hp_kv), _p,
                                  _p, _sz, _p],
             "hp_layer_decode": [C.POINTER(hp_dims), C.POINTER(hp_layer), _p, _i32, _i32, _p,
@@ -100,6 +109,8 @@ def lib():
         L.hp_kv_bytes.argtypes = [C.POINTER(hp_dims), _i32]
         L.hp_kv_bytes.restype = C.c_uint64
         L.hp_release_graphs.restype = None
+        L.hp_debug_set_capture.argtypes = [C.POINTER(hp_capture)]
+        L.hp_debug_set_capture.restype = _i32
         L.hp_profile.argtypes = [_i32]
         L.hp_profile.restype = _i32
         L.hp_profile_read.argtypes = [C.c_char_p, _sz]
@@ -283,22 +294,34 @@ def hp_tree_masks(parent: torch.Tensor, stream=None):
     return masks, err
 
 
-def hp_tree_prune(parent: torch.Tensor, verified: torch.Tensor, stream=None):
-    """parent int32 [b][q], verified int32 [b] (device) -> (new_parent, src, kept, err)."""
+def hp_decode_attention_ragged(b, q, h1, heads, qkv, prefix, max_prefix, kv: KVCache, masks=None,
+                               out=None, stream=None):
+    """hp_decode_attention with per-request prefix lengths (device int32 [b])."""
+    out = out if out is not None else torch.empty((b, q, h1), dtype=torch.float16, device=qkv.device)
+    c = kv.c()
+    _check(lib().hp_decode_attention_ragged(b, q, h1, heads, _ptr(qkv), _ptr(prefix), max_prefix,
+                                            _ptr(masks), C.byref(c), _ptr(out), _stream(stream)))
+    return out
+
+
+def hp_tree_prune(parent: torch.Tensor, verified: torch.Tensor, pos: int = 0, stream=None):
+    """parent int32 [b][q], verified int32 [b] (device), tree rows after a prefix of pos
+    rows -> (new_parent, src, prefix, kept, err), all device int32."""
     b, q = parent.shape
     new_parent = torch.empty((b, q), dtype=torch.int32, device=parent.device)
     src = torch.empty((b, q), dtype=torch.int32, device=parent.device)
+    prefix = torch.empty(b, dtype=torch.int32, device=parent.device)
     kept = torch.empty(b, dtype=torch.int32, device=parent.device)
     err = torch.empty(1, dtype=torch.int32, device=parent.device)
-    _check(lib().hp_tree_prune(b, q, _ptr(parent), _ptr(verified), _ptr(new_parent), _ptr(src),
-                               _ptr(kept), _ptr(err), _stream(stream)))
-    return new_parent, src, kept, err
+    _check(lib().hp_tree_prune(b, q, _ptr(parent), _ptr(verified), pos, _ptr(new_parent),
+                               _ptr(src), _ptr(prefix), _ptr(kept), _ptr(err), _stream(stream)))
+    return new_parent, src, prefix, kept, err
 
 
-def hp_kv_compact(b, q, h1, heads, pos, src, kept, kv: KVCache, stream=None):
+def hp_kv_compact(b, q, h1, heads, pos, src, prefix, kept, kv: KVCache, stream=None):
     c = kv.c()
-    _check(lib().hp_kv_compact(b, q, h1, heads, pos, _ptr(src), _ptr(kept), C.byref(c),
-                               _stream(stream)))
+    _check(lib().hp_kv_compact(b, q, h1, heads, pos, _ptr(src), _ptr(prefix), _ptr(kept),
+                               C.byref(c), _stream(stream)))
 
 
 # ------------------------------------------------------------------ layers
@@ -339,6 +362,20 @@ def hp_layer_decode(d: hp_dims, layer: Layer, t, pos, q, kv: KVCache, t_out, ws,
     lc, kc = layer.c(), kv.c()
     _check(lib().hp_layer_decode(C.byref(d), C.byref(lc), _ptr(t), pos, q, _ptr(masks),
                                  C.byref(kc), _ptr(t_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def hp_debug_set_capture(qkv=None, attn=None, x_out=None, hidden=None, off=False):
+    """Teacher-forcing diagnostics: later hp_layer_prefill / hp_layer_decode calls on
+    this thread copy their stored fp16 intermediates into these device tensors
+    (contiguous, M rows); off=True stops capturing."""
+    if off:
+        _check(lib().hp_debug_set_capture(None))
+        return
+    for t in (qkv, attn, x_out, hidden):
+        if t is not None:
+            _need(t, torch.float16, "capture buffer")
+    c = hp_capture(_ptr(qkv), _ptr(attn), _ptr(x_out), _ptr(hidden))
+    _check(lib().hp_debug_set_capture(C.byref(c)))
 
 
 def hp_run_block(d: hp_dims, layers, x, t_in, kvs, x_out, t_out, ws, flags=0, timing=False,

@@ -27,8 +27,11 @@
  *    (thread-local text).  HP_ERR_HIP reports a HIP runtime error at launch;
  *    errors raised later by the device surface at the caller's next sync.
  *  - binary16 tensors are IEEE 754 half precision; row-major throughout.
- *  - Results do not depend on gbs or on the schedule order: every row's sums
- *    are reduced in an order fixed by the matrix shapes alone.
+ *  - A product's rows are summed in an order fixed by (k, n) and by which
+ *    side of M = 144 rows the product falls on (M <= 144: the skinny decode
+ *    kernels; M > 144: the tiled kernel, another order).  Schedules whose
+ *    products stay on one side of that boundary give bitwise-equal results;
+ *    across it they differ by rounding only.
  *  - The device must be gfx950 (HP_ERR_DEVICE otherwise).
  */
 #ifndef HP_H_
@@ -189,6 +192,17 @@ hp_status hp_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, c
                               int32_t pos, const uint64_t* masks, const hp_kv* kv, void* out,
                               void* stream);
 
+/* hp_decode_attention with a prefix length per request, as after tree
+ * pruning (hp_tree_prune): query i of request r reads rows [0, P) and each
+ * row P + u with bit u of masks[r][i] set (masks == NULL: a chain, rows
+ * P .. P + i), P = prefix[r] (device int32 [b]) clamped to [0, max_prefix].
+ * Requires max_prefix + q <= kv->cap; other arguments as in
+ * hp_decode_attention. */
+hp_status hp_decode_attention_ragged(int32_t b, int32_t q, int32_t h1, int32_t heads,
+                                     const void* qkv, const int32_t* prefix, int32_t max_prefix,
+                                     const uint64_t* masks, const hp_kv* kv, void* out,
+                                     void* stream);
+
 /* Top-K sparse decode attention ([FlexGen] section 5, sparse attention): for
  * request r's new token (its K/V already appended at row pos), the scores
  * q . k_j over cache rows j in [0, pos] are formed through the stored format,
@@ -212,30 +226,43 @@ hp_status hp_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* m
                         int32_t* err, void* stream);
 
 /* [SpecPipe] 2.2.1 sub-tree pruning (Fig. 5-b) and 2.2.2 (Fig. 8): when
- * token verified[r] of request r's BFS tree of q tokens is verified, the
- * request keeps the tokens on its path to the root (the verified path,
- * whose cache rows every kept token sees) and its subtree, in BFS order.
- * parent: device int32 [b][q] (rules of hp_tree_masks); verified: device
- * int32 [b].  Outputs (device int32): kept[r] = number of kept tokens;
- * src[r][j] = old index of kept token j (j < kept[r], else -1);
- * new_parent[r][j] = new index of its parent (-1 for the root); entries
- * j >= kept[r] are filler leaves (the last kept token's parent, or 0 when
- * one token is kept), so new_parent is again a valid BFS parent array.  A
- * request with an invalid parent array or verified index outside [0, q)
- * keeps nothing (kept 0, new_parent a star, src -1); err (device int32, or
- * NULL) is set to the number of such requests.  q in [1, 64]; one
- * kernel launch (one wave per request). */
+ * token u = verified[r] of request r's BFS tree of q tokens (cache rows
+ * pos .. pos + q - 1 after a prefix of pos rows) is verified, the tree keeps
+ * u and its descendants (column u of the mask matrix), in BFS order, and u
+ * becomes its root; the rows of the verified path above u (the root down to
+ * u's parent) stay in the cache as committed prefix.  parent: device int32
+ * [b][q] (rules of hp_tree_masks); verified: device int32 [b].  Outputs
+ * (device int32):
+ *   prefix[r] = pos + depth, depth = number of u's ancestors: the new
+ *               prefix length (the path rows are committed);
+ *   kept[r]   = size of the new tree (u's subtree, u included);
+ *   src[r][j] = for j < depth + kept[r], the old tree index of the token
+ *               whose cache row goes to row pos + j: the path (root first),
+ *               then the new tree's tokens in order; -1 beyond;
+ *   new_parent[r][t] = for t < kept[r], the new index of token t's parent
+ *               (-1 for u, at t = 0); entries t >= kept[r] are filler leaves
+ *               (the last kept token's parent, or 0 when u is alone), so
+ *               new_parent is again a valid BFS parent array.
+ * Token t of the new tree is old token src[r][depth + t]; after
+ * hp_kv_compact its K/V rows sit at prefix[r] + t.  A request with an invalid
+ * parent array or verified index outside [0, q) keeps nothing (prefix = pos,
+ * kept 0, new_parent a star, src -1); err (device int32, or NULL) is set to
+ * the number of such requests.  q in [1, 64]; one kernel launch (one wave
+ * per request). */
 hp_status hp_tree_prune(int32_t b, int32_t q, const int32_t* parent, const int32_t* verified,
-                        int32_t* new_parent, int32_t* src, int32_t* kept, int32_t* err,
-                        void* stream);
+                        int32_t pos, int32_t* new_parent, int32_t* src, int32_t* prefix,
+                        int32_t* kept, int32_t* err, void* stream);
 
-/* Moves one layer's kept tree rows into place after hp_tree_prune: for
- * request r and every head, cache row pos + j (j < kept[r]) takes the K and
- * V rows (codes and scale/min, or fp16) of row pos + src[r][j].  Rows
- * [0, pos) and [pos + kept[r], pos + q) are not touched.  src, kept: device
- * int32 as written by hp_tree_prune.  Requires pos + q <= kv->cap. */
+/* Moves one layer's surviving rows into place after hp_tree_prune: for
+ * request r and every head, cache row pos + j, j < prefix[r] - pos + kept[r],
+ * takes the K and V rows (codes and scale/min, or fp16) of row
+ * pos + src[r][j].  Rows [0, pos) and the rows after the moved ones (up to
+ * pos + q) are not touched.  src, prefix, kept: device int32 as written by
+ * hp_tree_prune (a count outside [0, q] is clamped to it).  Requires
+ * pos + q <= kv->cap. */
 hp_status hp_kv_compact(int32_t b, int32_t q, int32_t h1, int32_t heads, int32_t pos,
-                        const int32_t* src, const int32_t* kept, const hp_kv* kv, void* stream);
+                        const int32_t* src, const int32_t* prefix, const int32_t* kept,
+                        const hp_kv* kv, void* stream);
 
 /* ------------------------------------------------------------- layers */
 /* Workspace for hp_layer_prefill / hp_layer_decode / hp_run_block with these
@@ -256,6 +283,28 @@ hp_status hp_layer_decode(const hp_dims* d, const hp_layer* w, const void* t, in
                           int32_t q, const uint64_t* masks, const hp_kv* kv, void* t_out,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* Diagnostics for teacher-forced checks: the fp16 tensors a layer stores
+ * between its stages ([FlexGen] background section: Q/K/V, the attention
+ * output, x_Out and the MLP hidden relu(x_Out w_1); section 5: K/V are
+ * quantised from the stored fp16 rows).  While a capture is set on the
+ * calling thread, every hp_layer_prefill and hp_layer_decode call on that
+ * thread copies them, after the layer, into the given device buffers
+ * (M = b s rows for prefill, b q for decode; any pointer may be NULL):
+ *   qkv    half [M][3 h1]  (Q | K | V, the rows appended to the cache),
+ *   attn   half [M][h1]    (softmax(Q K^T / sqrt(d)) V),
+ *   x_out  half [M][h1]    (attn w_O + x),
+ *   hidden half [M][h2]    (relu(x_out w_1)).
+ * The buffers must hold M rows; the copies are enqueued on the layer's
+ * stream.  hp_debug_set_capture(NULL) turns capturing off.  hp_run_block
+ * never captures. */
+typedef struct {
+  void* qkv;
+  void* attn;
+  void* x_out;
+  void* hidden;
+} hp_capture;
+hp_status hp_debug_set_capture(const hp_capture* c);
+
 /* --------------------------------------------------------- block schedule */
 enum {
   HP_GRAPH = 1,      /* capture one decode column as a hipGraph, replay it n times */
@@ -268,7 +317,10 @@ enum {
   HP_DIAGONAL = 16   /* diagonal block schedule ([FlexGen] appendix A.2, Fig. 5):
                         GPU batch k runs step it - k of iteration it (0 = its
                         prefill), layer-major over the batches of each
-                        iteration; results equal the zig-zag block's.  Batch k
+                        iteration; results equal the zig-zag block's bit for
+                        bit when each product of the two schedules falls on
+                        the same side of M = 144 rows (always for b <= 144),
+                        within rounding otherwise.  Batch k
                         keeps its cache in slot k mod min(b / gbs, n + 1), so
                         kv[j] needs only that many GPU batches of requests.
                         Eager launches: not with HP_GRAPH, HP_ROW_BY_ROW or

@@ -60,7 +60,7 @@ def lib():
         L.or_tree_masks.restype = _int
         L.or_tree_masks.argtypes = [_p, _int, _p]
         L.or_tree_prune.restype = _int
-        L.or_tree_prune.argtypes = [_p, _int, _int, _p, _p]
+        L.or_tree_prune.argtypes = [_p, _int, _int, _p, _p, _p]
         L.or_run_block.argtypes = [_int] * 9 + [_p, _p, _p, _int, _int, _p, _p, _p, _p, _p, _p]
         _lib = L
     return _lib
@@ -193,22 +193,28 @@ def tree_masks(parent) -> np.ndarray:
 
 
 def tree_prune(parent, u: int):
-    """[SpecPipe] sub-tree pruning: (new_parent [nq], src [nq], kept) for verified token u."""
+    """[SpecPipe] sub-tree pruning for verified token u: (new_parent [nq], src [nq], kept,
+    depth).  kept = size of u's subtree (the new tree, u at index 0); depth = length of
+    the verified path above u (cache rows committed to the prefix); src[j], j < depth +
+    kept, = old index of the token whose row goes to position j after the old prefix."""
     p = _c(parent, np.int32)
     new_parent = np.zeros(p.shape[0], np.int32)
     src = np.zeros(p.shape[0], np.int32)
-    kept = lib().or_tree_prune(_ptr(p), p.shape[0], int(u), _ptr(new_parent), _ptr(src))
+    depth = np.zeros(1, np.int32)
+    kept = lib().or_tree_prune(_ptr(p), p.shape[0], int(u), _ptr(new_parent), _ptr(src),
+                               _ptr(depth))
     if kept < 0:
         raise ValueError("invalid parent array or verified index")
-    return new_parent, src, kept
+    return new_parent, src, kept, int(depth[0])
 
 
-def kv_compact(kv, pos: int, src, kept):
-    """Moves kept tree rows into place: for request r, rows pos + j (j < kept[r]) of every
-    head take rows pos + src[r][j] (K and V, codes and scale/min); other rows untouched."""
+def kv_compact(kv, pos: int, src, count):
+    """Moves the rows that survive pruning into place: for request r, rows pos + j
+    (j < count[r]) of every head take rows pos + src[r][j] (K and V, codes and
+    scale/min); other rows untouched."""
     for r in range(kv.b):
-        idx = pos + np.asarray(src[r][:kept[r]], np.int64)
-        dst = slice(pos, pos + int(kept[r]))
+        idx = pos + np.asarray(src[r][:count[r]], np.int64)
+        dst = slice(pos, pos + int(count[r]))
         for arr in (kv.k, kv.v, kv.ksm, kv.vsm):
             if arr is not None:
                 arr[r][:, dst] = arr[r][:, idx].copy()

@@ -399,40 +399,48 @@ int or_tree_masks(const int32_t* parent, int nq, uint64_t* mask) {
 }
 
 // ------------------------------------------------------------ tree pruning
-// [SpecPipe] 2.2.1 (sub-tree pruning, Fig. 5-b) and 2.2.2 (Fig. 8): once
-// token u is verified, the token arrays keep the subtree rooted at u (the
-// tokens whose column-u entry of M is set: u and its descendants), and the
-// cache keeps the rows of the verified path, u's ancestors, which every kept
-// token sees.  Kept tokens are the ancestors of u and u's subtree, in their
-// BFS order; the parent of a kept token is its old parent's new index.
-// Slots j >= kept get filler leaves (parent of the last kept token, or 0
-// when only one token is kept) so that new_parent stays a valid BFS array.
-// src[j] = old index of kept token j.  Returns the kept count, or -1 when
-// the parent array is invalid or u is outside [0, nq).
-int or_tree_prune(const int32_t* parent, int nq, int u, int32_t* new_parent, int32_t* src) {
+// [SpecPipe] 2.2.1 (sub-tree pruning, Fig. 5-b) and 2.2.2 (Fig. 8).  When
+// token u is verified, column u of the mask matrix M selects the tokens whose
+// path to the root passes through u: u and its descendants.  The token arrays
+// keep exactly those tokens, in their BFS order, and the new mask makes u the
+// root.  The cache keeps the rows of the verified path above u (the root down
+// to u's parent, found as row u of M without u itself): they leave the tree
+// and join the committed prefix.
+// Outputs: *depth = length of that path (rows committed to the prefix);
+// src[j] for j < depth + kept = old index of the token whose cache row goes
+// to position j after the old prefix: the path (root first), then the kept
+// tokens; src[j] = -1 beyond.  new_parent[t] for t < kept = the new index of
+// kept token t's parent (-1 for u); slots t >= kept hold filler leaves (the
+// parent of the last kept token, or 0 when u is the only one) so that the
+// array stays a valid BFS parent array.  Returns kept, or -1 when the parent
+// array is invalid or u is outside [0, nq).
+int or_tree_prune(const int32_t* parent, int nq, int u, int32_t* new_parent, int32_t* src,
+                  int32_t* depth) {
   uint64_t mask[64];
   if (or_tree_masks(parent, nq, mask) != 0 || u < 0 || u >= nq) return -1;
+  // the verified path above u: row u of M, less u itself, in index order
+  int path = 0;
+  for (int i = 0; i < u; ++i)
+    if ((mask[u] >> i) & 1ull) src[path++] = i;
+  // the kept tokens: column u of M, in index (BFS) order, u first
   int newidx[64];
   int kept = 0;
   for (int i = 0; i < nq; ++i) {
-    const bool ancestor_of_u = (mask[u] >> i) & 1ull;  // i on the path from u to the root
-    const bool in_subtree = (mask[i] >> u) & 1ull;     // u on the path from i to the root
     newidx[i] = -1;
-    if (ancestor_of_u || in_subtree) {
+    if ((mask[i] >> u) & 1ull) {
       newidx[i] = kept;
-      src[kept] = i;
+      src[path + kept] = i;
       ++kept;
     }
   }
-  for (int j = 0; j < kept; ++j) {
-    const int p = parent[src[j]];
-    new_parent[j] = p < 0 ? -1 : newidx[p];
+  for (int t = 0; t < kept; ++t) {
+    const int i = src[path + t];
+    new_parent[t] = i == u ? -1 : newidx[parent[i]];
   }
   const int fill = kept == 1 ? 0 : new_parent[kept - 1];
-  for (int j = kept; j < nq; ++j) {
-    new_parent[j] = fill;
-    src[j] = -1;
-  }
+  for (int t = kept; t < nq; ++t) new_parent[t] = fill;
+  for (int j = path + kept; j < nq; ++j) src[j] = -1;
+  *depth = path;
   return kept;
 }
 

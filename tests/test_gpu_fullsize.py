@@ -150,7 +150,8 @@ def _tree_case(hp, orc):
     masks, err = hp.hp_tree_masks(dev(parents.astype(np.int32)))
     mref = np.stack([orc.tree_masks(p) for p in parents])
     assert np.array_equal(host(masks).view(np.uint64), mref) and int(host(err)[0]) == 0
-    kv = hp.KVCache(c["kv_fmt"], b, heads, P + q, D)
+    cap = P + 2 * q  # after pruning, the next tree starts after a longer prefix
+    kv = hp.KVCache(c["kv_fmt"], b, heads, cap, D)
     pre = torch.zeros((b, P, 3 * h1), dtype=torch.float16, device="cuda")
     pre[:, :, h1:2 * h1].copy_(dev(kp))
     pre[:, :, 2 * h1:].copy_(dev(vp))
@@ -159,7 +160,7 @@ def _tree_case(hp, orc):
     qt = dev(qkv_t)
     hp.hp_kv_append(b, q, h1, heads, qt, P, kv)
     out = host(hp.hp_decode_attention(b, q, h1, heads, qt, P, kv, masks=masks))
-    kref = orc.KV(c["kv_fmt"], b, heads, P + q, D)
+    kref = orc.KV(c["kv_fmt"], b, heads, cap, D)
     orc.kv_append(kref, kp, vp, 0)
     orc.kv_append(kref, qkv_t[:, :, h1:2 * h1], qkv_t[:, :, 2 * h1:], P)
     _check_cache(orc, kv, rows, kref, 0, P + q, True, "tree cache")
@@ -187,39 +188,48 @@ def test_fullsize_tree_attention(hp, orc):
 
 def test_fullsize_tree_pruning(hp, orc):
     """The tree workload after verification ([SpecPipe] 2.2.1 sub-tree pruning,
-    2.2.2): one verified token per request; plans and the whole compacted int4
-    cache (all 64 heads) bit-exact against the oracle; attention of the kept
-    tokens over the compacted cache with the new masks on sampled heads."""
+    2.2.2): one verified token per request; its subtree stays as the new tree with
+    it as root, the path above it commits to that request's prefix.  Plans and the
+    whole compacted int4 cache (all 64 heads) bit-exact against the oracle;
+    attention of the kept tokens over the compacted cache, each request with its own
+    prefix length and the new masks, on sampled heads."""
     c, kv, kref, qkv_t, qt, parents, masks, mref, out = _tree_case(hp, orc)
     b, h1, heads, P, q = c["b"], c["h1"], c["heads"], c["prefix"], c["q"]
     D = h1 // heads
     seed = synth.seed_for(5)
     verified = (synth.words(seed, 7000, 0, b) % np.uint64(q)).astype(np.int32)
-    new_parent, src, kept, err = hp.hp_tree_prune(dev(parents.astype(np.int32)), dev(verified))
+    new_parent, src, prefix, kept, err = hp.hp_tree_prune(dev(parents.astype(np.int32)),
+                                                          dev(verified), P)
     assert int(host(err)[0]) == 0
-    npar, srch, kepth = host(new_parent), host(src), host(kept)
+    npar, srch, kepth, preh = host(new_parent), host(src), host(kept), host(prefix)
     for r in range(b):
-        rp, rs, rk = orc.tree_prune(parents[r], int(verified[r]))
-        assert int(kepth[r]) == rk and np.array_equal(npar[r], rp) and np.array_equal(srch[r], rs)
-    hp.hp_kv_compact(b, q, h1, heads, P, src, kept, kv)
-    orc.kv_compact(kref, P, srch, kepth)
+        rp, rs, rk, depth = orc.tree_prune(parents[r], int(verified[r]))
+        assert int(kepth[r]) == rk and int(preh[r]) == P + depth
+        assert np.array_equal(npar[r], rp) and np.array_equal(srch[r], rs)
+    hp.hp_kv_compact(b, q, h1, heads, P, src, prefix, kept, kv)
+    orc.kv_compact(kref, P, srch, preh - P + kepth)
     for name, oname in (("k", "k"), ("v", "v"), ("k_sm", "ksm"), ("v_sm", "vsm")):
         assert np.array_equal(host(getattr(kv, name)), getattr(kref, oname)), name
     new_masks, e2 = hp.hp_tree_masks(new_parent)
     assert int(host(e2)[0]) == 0
     q2 = np.zeros_like(qkv_t)
+    kept_old = []
     for r in range(b):
-        q2[r, :kepth[r]] = qkv_t[r, srch[r, :kepth[r]]]
-    out2 = host(hp.hp_decode_attention(b, q, h1, heads, dev(q2), P, kv, masks=new_masks))
-    K, V = kref.values("k", P + q), kref.values("v", P + q)
+        dpt = int(preh[r]) - P
+        kept_old.append(srch[r, dpt:dpt + kepth[r]])
+        q2[r, :kepth[r]] = qkv_t[r, kept_old[r]]
+    out2 = host(hp.hp_decode_attention_ragged(b, q, h1, heads, dev(q2), prefix, P + q - 1, kv,
+                                              masks=new_masks))
+    cap = kref.cap
+    K, V = kref.values("k", cap), kref.values("v", cap)
     for r, h in ((0, 0), (1, 17), (2, 33), (3, 63), (4, 5), (5, 40), (6, 21), (7, 58)):
-        k = int(kepth[r])
+        k, P2 = int(kepth[r]), int(preh[r])
         sl = slice(h * D, (h + 1) * D)
         m = orc.tree_masks(npar[r])[:k]
-        ref = orc.attention(q2[r, :k, sl], K[r, h], V[r, h], [P] * k, m, P)
+        ref = orc.attention(q2[r, :k, sl], K[r, h], V[r, h], [P2] * k, m, P2)
         assert_close(out2[r, :k, sl], ref, what=f"pruned tree attention r{r} h{h}")
         # the kept tokens' outputs equal their outputs before pruning, within rounding
-        assert_close(out2[r, :k, sl], out[r, srch[r, :k], sl], what=f"before/after r{r} h{h}")
+        assert_close(out2[r, :k, sl], out[r, kept_old[r], sl], what=f"before/after r{r} h{h}")
 
 
 def test_fullsize_diagonal_schedule(hp):
