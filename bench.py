@@ -143,6 +143,165 @@ def graph_ms(torch, stream, fn, reps=3):
     return e0.elapsed_time(e1) / reps
 
 
+def refill_finite(hp, torch, stream, c, kvs):
+    """Overwrites cache rows [0, s + n) of every layer with seeded finite K/V rows,
+    N(0, (0.02 sqrt(h1))^2) (the scale of x w for x ~ N(0, 1), w ~ N(0, 0.02^2)),
+    appended through hp_kv_append.  The block's own caches are not finite: the page's
+    layer has no LayerNorm, so its residual stream overflows fp16 after a few layers
+    and later layers cache non-finite rows."""
+    b, h1, H = c["b"], c["h1"], c["heads"]
+    rows = c["s"] + c["n"]
+    g = torch.Generator(device="cuda")
+    qkv = torch.empty((b, rows, 3 * h1), dtype=torch.float16, device="cuda")
+    for j, kv in enumerate(kvs):
+        g.manual_seed(7000 + j)
+        qkv.normal_(0.0, 0.02 * h1 ** 0.5, generator=g)
+        hp.hp_kv_append(b, rows, h1, H, qkv, 0, kv, stream=stream)
+    del qkv
+    stream.synchronize()
+
+
+def finite_tokens(torch, c, seed=17):
+    """One seeded N(0, 1) token embedding per layer and request: [l][b][1][h1]."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn((c["l"], c["b"], 1, c["h1"]), generator=g, device="cuda").half()
+
+
+def decode_column_finite(hp, torch, stream, c, d, layers, kvs, ws):
+    """One decode column (every layer, one token per request) at the block's mean
+    cache length T = s + n/2, on finite data: each layer reads its own seeded N(0, 1)
+    input and a cache of finite rows (refill_finite), so nothing overflows; replayed
+    from a HIP graph like the block's column.  Its time against the block's decode
+    time per step shows whether the non-finite values of the block move its timing."""
+    b, l = c["b"], c["l"]
+    T = c["s"] + c["n"] // 2
+    tin = finite_tokens(torch, c)
+    tout = torch.empty_like(tin)
+
+    def run():
+        for j in range(l):
+            hp.hp_layer_decode(d, layers[j], tin[j], T - 1, 1, kvs[j], tout[j], ws, stream=stream)
+
+    ms = graph_ms(torch, stream, run)
+    finite = bool(torch.isfinite(tout.float()).all().item())
+    return {"column_ms": ms, "tokens_per_s": b / (ms / 1e3), "outputs_finite": finite, "T": T,
+            "work": "l x hp_layer_decode at cache length T, finite inputs and caches, graph replay"}
+
+
+def prefill_products_finite(hp, torch, stream, c, layers):
+    """The four prefill products of layer 0 at M = b*s ([FlexGen] background section:
+    x w_QKV, a w_O + x, relu(x_Out w_1), h w_2 + x_Out) on finite seeded inputs, each
+    launch event-timed through hp_profile: the tiled MFMA kernel's time on finite data,
+    beside the block's (whose later layers carry non-finite activations)."""
+    b, s, h1, h2 = c["b"], c["s"], c["h1"], c["h2"]
+    M = b * s
+    ly = layers[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(19)
+    ldh = h2 + 64 if h2 % 8192 == 0 else h2  # the block's padded stride for the hidden
+    x = torch.randn((M, h1), generator=g, device="cuda").half()
+    hid = torch.randn((M, ldh), generator=g, device="cuda").half().relu_()[:, :h2]
+    out3 = torch.empty((M, 3 * h1), dtype=torch.float16, device="cuda")
+    out1 = torch.empty((M, h1), dtype=torch.float16, device="cuda")
+    outh = torch.empty((M, ldh), dtype=torch.float16, device="cuda")[:, :h2]
+    need = max(hp.hp_gemm_workspace_bytes(M, m.k, m.n, m.fmt) for m in (ly.wqkv, ly.wo, ly.w1, ly.w2))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    prods = [(x, ly.wqkv, None, False, out3), (x, ly.wo, x, False, out1),
+             (x, ly.w1, None, True, outh), (hid, ly.w2, x, False, out1)]
+    for inp, w, res, relu, out in prods:  # warm-up
+        hp.hp_gemm(inp, w, res=res, relu=relu, out=out, ws=ws, stream=stream)
+    stream.synchronize()
+    hp.hp_profile(True)
+    reps = 2
+    for _ in range(reps):
+        for inp, w, res, relu, out in prods:
+            hp.hp_gemm(inp, w, res=res, relu=relu, out=out, ws=ws, stream=stream)
+    stream.synchronize()
+    hp.hp_profile(False)
+    prof = hp.hp_profile_read()
+    finite = all(bool(torch.isfinite(o.float()).all().item()) for o in (out3, out1))
+    cnt, tot = prof.get("gemm_f16_tiled", (0, 0.0))
+    res = {"outputs_finite": finite, "kernels": {k: {"launches": v[0], "total_ms": v[1]}
+                                                 for k, v in prof.items()}}
+    if cnt:
+        flops = reps * layer_flops(c, M)
+        res.update(kernel="gemm_f16_tiled", avg_launch_ms=tot / cnt,
+                   tflops=flops / (tot / 1e3) / 1e12,
+                   frac_mfma=flops / (tot / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS)
+    del x, hid, out3, out1, outh, ws
+    return res
+
+
+def quant_kernels(hp, torch, stream, c, reps=10):
+    """The int4 group-64 coder ([FlexGen] section 5) at its two uses: hp_quantize_g64
+    on a weight of the 175B shape (w1, 12288 x 49152) and of this configuration, and
+    hp_kv_append at the prefill shape (b*s tokens) and the decode shape (b tokens),
+    event-timed over `reps` launches on finite seeded data.  HBM bytes per element:
+    2 read + 0.5625 written (codes + fp16 scale/min per group of 64)."""
+    b, s, h1, H = c["b"], c["s"], c["h1"], c["heads"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(23)
+
+    def ev_ms(fn, r):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(r):
+            fn()
+        e1.record(stream)
+        stream.synchronize()
+        return e0.elapsed_time(e1) / r
+
+    out = {"bound": "hbm", "work": "elements x (2 + 0.5625) bytes per launch"}
+    for name, (k, n) in (("quantize_175b_w1", (12288, 49152)),
+                         ("quantize_w1", (c["h1"], c["h2"]))):
+        w = (torch.randn((k, n), generator=g, device="cuda") * 0.02).half()
+        codes = torch.empty((k, n // 2), dtype=torch.uint8, device="cuda")
+        sm = torch.empty((k, n // 64, 2), dtype=torch.int16, device="cuda")
+        ms = ev_ms(lambda: hp.lib().hp_quantize_g64(w.data_ptr(), k, n, codes.data_ptr(),
+                                                    sm.data_ptr(), stream.cuda_stream), reps)
+        by = k * n * 2.5625
+        out[name] = {"shape": [k, n], "avg_us": ms * 1e3, "gbs": by / (ms / 1e3) / 1e9,
+                     "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del w, codes, sm
+    if c["fmt"] == 1:
+        kv = hp.KVCache(1, b, H, s + 1, h1 // H)
+        qkv = (torch.randn((b, s, 3 * h1), generator=g, device="cuda") * 0.02 * h1 ** 0.5).half()
+        ms = ev_ms(lambda: hp.hp_kv_append(b, s, h1, H, qkv, 0, kv, stream=stream), reps)
+        by = 2 * b * s * h1 * 2.5625
+        out["kv_append_prefill"] = {"tokens": b * s, "avg_us": ms * 1e3,
+                                    "gbs": by / (ms / 1e3) / 1e9,
+                                    "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+        q1 = qkv[:, :1].contiguous()
+        ms = ev_ms(lambda: hp.hp_kv_append(b, 1, h1, H, q1, s, kv, stream=stream), 5 * reps)
+        out["kv_append_decode"] = {"tokens": b, "avg_us": ms * 1e3,
+                                   "note": "launch-bound (%.1f MB per launch)"
+                                           % (2 * b * h1 * 2.5625 / 1e6)}
+        del kv, qkv, q1
+    return out
+
+
+def tiny_block(hp, torch, stream, reps=5):
+    """The Tiny configuration (l = 2, h1 = 256, b = 4, s = 32, n = 8, int4): a whole
+    block, decode columns replayed from a HIP graph against launched one kernel at a
+    time; launch latency bounds it, so the figure is microseconds per decode step."""
+    c = CONFIGS["tiny"]
+    d, layers, x, t_in, kvs, ws, x_out, t_out = setup(c, CONFIG_SEED["tiny"], hp, torch)
+    res = {}
+    for name, flags in (("graph", hp.HP_GRAPH), ("eager", 0)):
+        hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws, flags, timing=True,
+                        stream=stream)
+        runs = sorted(hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws, flags,
+                                      timing=True, stream=stream) for _ in range(reps))
+        pre, dec = runs[len(runs) // 2]
+        res[name] = {"prefill_us": pre * 1e3, "decode_us_per_step": dec * 1e3 / c["n"],
+                     "decode_tokens_per_s": c["b"] * c["n"] / (dec / 1e3)}
+    res["finite"] = bool(torch.isfinite(t_out.float()).all().item())
+    res["work"] = "median of %d blocks; decode time / n steps" % reps
+    return res
+
+
 def decode_products(hp, torch, stream, c, layers):
     """The four decode-phase products of a layer at M = b ([FlexGen] background
     section: x·w_QKV, ·w_O + residual, relu(·w_1), ·w_2 + residual), each run once per
@@ -394,39 +553,61 @@ def main():
         prof = hp.hp_profile_read()
         nonfinite = int((~torch.isfinite(t_out.float())).sum().item())
 
-        # decode-phase kernels: one eager decode column (cache rows already
-        # filled by the timed blocks), each launch timed with HIP events; the
-        # column is queued behind a spin kernel so that no event pair spans
-        # a wait for the host's next launch
+        # every measurement below runs on finite data: the block's caches are
+        # refilled with finite rows and every layer reads its own finite input
+        log("finite caches")
+        refill_finite(hp, torch, stream, c, kvs)
+        # decode-phase kernels: one eager decode column, each launch timed with
+        # HIP events; the column is queued behind a spin kernel so that no event
+        # pair spans a wait for the host's next launch
         T = c["s"] + c["n"] // 2
-        tcur = t_in[0].contiguous()
-        tnext = torch.empty_like(tcur)
+        tin = finite_tokens(torch, c)
+        tnext = torch.empty_like(tin[0])
         held = hold_stream(torch, stream)
         hp.hp_profile(True)
         for j in range(c["l"]):
-            hp.hp_layer_decode(d, layers[j], tcur, T - 1, 1, kvs[j], tnext, ws, stream=stream)
-            tcur, tnext = tnext, tcur
+            hp.hp_layer_decode(d, layers[j], tin[j], T - 1, 1, kvs[j], tnext, ws, stream=stream)
         dec_queued_ahead = not held.query()
         stream.synchronize()
         hp.hp_profile(False)
         dprof = hp.hp_profile_read()
+        del tin, tnext
+        log("decode column (finite)")
+        dcol = decode_column_finite(hp, torch, stream, c, d, layers, kvs, ws)
+        log("decode products")
         dgemm = decode_products(hp, torch, stream, c, layers)
+        log("sparse attention (finite caches)")
         sparse = sparse_attention(hp, torch, stream, c, kvs, args.config)
+        log("quantiser and KV append")
+        qk = quant_kernels(hp, torch, stream, c)
+        log("prefill products (finite)")
+        pgemm = prefill_products_finite(hp, torch, stream, c, layers)
         topk_block = None
         if not args.no_topk_block and c["s"] + c["n"] <= 4096:
             # the same block with 10% Top-K attention in every decode column
+            log("Top-K block")
             tk = hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws,
                                  hp.HP_GRAPH | hp.HP_TOPK10, timing=True, stream=stream)
             tk = hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws,
                                  hp.HP_GRAPH | hp.HP_TOPK10, timing=True, stream=stream)
+            # the same column on finite data, from the finite per-layer times: the
+            # dense column with each layer's dense attention replaced by Top-K
+            est = dcol["column_ms"] + c["l"] * (sparse["topk_us"] - sparse["dense_us"]) / 1e3
             topk_block = {"decode_ms": tk[1], "prefill_ms": tk[0],
                           "tokens_per_s": c["b"] * c["n"] / (tk[1] / 1e3),
+                          "data": "the block's own activations: non-finite after the first "
+                                  "layers (no LayerNorm), so the Top-K selection there runs on "
+                                  "NaN scores and this figure is not a finite-data timing",
+                          "finite_estimate_tokens_per_s": c["b"] / (est / 1e3),
+                          "finite_estimate": "finite decode column - l x (dense - Top-K "
+                                             "attention on finite caches)",
                           "work": "one block as timed above (second run, graph cached) with "
                                   "HP_TOPK10: ceil(T/10) rows per (request, head) in decode"}
         diag = None
         if not args.no_diagonal:
             # the same requests under the diagonal block schedule (eager launches;
             # prefill and decode interleave, so only the whole schedule is timed)
+            log("diagonal block")
             nslot = min(c["b"] // c["gbs"], c["n"] + 1)
             td = hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws, hp.HP_DIAGONAL,
                                  timing=True, stream=stream)
@@ -434,6 +615,8 @@ def main():
                     "kv_GB": nslot * c["gbs"] / c["b"] * kvbytes / 1e9,
                     "iterations": c["b"] // c["gbs"] + c["n"]}
         tree = None if args.no_tree else tree_attention(hp, torch, stream)
+        log("tiny block")
+        tiny = tiny_block(hp, torch, stream)
 
     b, n, s, l = c["b"], c["n"], c["s"], c["l"]
     K = args.steps
@@ -513,11 +696,19 @@ def main():
                            if args.config == "opt-175b-int4" else None),
         "resident_GB": {"weights": wbytes / 1e9, "kv": kvbytes / 1e9},
         "nonfinite_decode_outputs": nonfinite,
+        "nonfinite_note": "the page's layer has no LayerNorm, so the stacked residual stream "
+                          "overflows fp16 after a few layers: every decode output of the "
+                          "block is non-finite.  decode_column_finite times the same column "
+                          "on finite data; all other sections below run on finite data",
         "roofline": roof,
+        "decode_column_finite": dict(dcol, block_column_ms=dec_ms / n),
         "decode_kernels": dec,
         "decode_kernels_queued_ahead": dec_queued_ahead,
         "decode_gemm": dgemm,
         "sparse_attention": sparse,
+        "quant_kernels": qk,
+        "prefill_gemm_finite": dict(pgemm, block_avg_launch_ms=roof.get("avg_launch_ms")),
+        "tiny_block": tiny,
         "topk10_block": topk_block,
         "diagonal_block": None if diag is None else dict(
             diag, tokens_per_s_incl_prefill=b * n / (diag["total_ms"] / 1e3),

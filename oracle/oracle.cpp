@@ -164,24 +164,28 @@ void or_dequantize_g64(const uint8_t* codes, const uint16_t* sm, i64 rows, i64 c
 // order in double; act is relu or identity; res may be absent.
 void or_gemm(const uint16_t* x, i64 ldx, const uint16_t* w, i64 M, i64 K, i64 N,
              const uint16_t* res, i64 ldr, int relu, uint16_t* y, i64 ldy) {
-  std::vector<double> wd((size_t)(K * N));
-#pragma omp parallel for schedule(static)
-  for (i64 k = 0; k < K; ++k)
-    for (i64 n = 0; n < N; ++n) wd[(size_t)(k * N + n)] = or_h2f(w[k * N + n]);
+  // Work is split over blocks of 256 output columns (each block takes all M
+  // rows); every output still sums its K products in ascending k.
+  const i64 NB = 256, nblk = (N + NB - 1) / NB;
 #pragma omp parallel for schedule(dynamic, 1)
-  for (i64 m = 0; m < M; ++m) {
-    std::vector<double> acc((size_t)N, 0.0);
+  for (i64 blk = 0; blk < nblk; ++blk) {
+    const i64 n0 = blk * NB, nn = std::min(NB, N - n0);
+    std::vector<double> acc((size_t)(M * nn), 0.0), wk((size_t)nn);
     for (i64 k = 0; k < K; ++k) {
-      const double a = or_h2f(x[m * ldx + k]);
-      const double* wr = wd.data() + (size_t)(k * N);
-      for (i64 n = 0; n < N; ++n) acc[(size_t)n] += a * wr[n];
+      for (i64 n = 0; n < nn; ++n) wk[(size_t)n] = or_h2f(w[k * N + n0 + n]);
+      for (i64 m = 0; m < M; ++m) {
+        const double a = or_h2f(x[m * ldx + k]);
+        double* am = acc.data() + (size_t)(m * nn);
+        for (i64 n = 0; n < nn; ++n) am[n] += a * wk[(size_t)n];
+      }
     }
-    for (i64 n = 0; n < N; ++n) {
-      double v = acc[(size_t)n];
-      if (relu) v = v > 0.0 ? v : 0.0;
-      if (res) v += or_h2f(res[m * ldr + n]);
-      y[m * ldy + n] = or_d2h(v);
-    }
+    for (i64 m = 0; m < M; ++m)
+      for (i64 n = 0; n < nn; ++n) {
+        double v = acc[(size_t)(m * nn + n)];
+        if (relu) v = v > 0.0 ? v : 0.0;
+        if (res) v += or_h2f(res[m * ldr + n0 + n]);
+        y[m * ldy + n0 + n] = or_d2h(v);
+      }
   }
 }
 

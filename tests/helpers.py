@@ -34,29 +34,6 @@ def assert_close(gpu, ref, tol=TOL, what=""):
     return float(err.max()) if err.size else 0.0
 
 
-def assert_close_rowscale(gpu, ref, tol=TOL, what=""):
-    """assert_close for whole-layer outputs at the full OPT shapes, with the floor
-    max(1, |ref|) raised to max(1, |ref|, rms(ref row) / 4).  The layer stores
-    fp16 at every intermediate (x, Q/K/V, the attention output, x_Out, the MLP
-    hidden) and int4 codes of the new K/V row; one rounding step or one code
-    level there, amplified by a peaked softmax and the MLP fan-in, moves an
-    output by up to ~3e-3 of its row's rms.  Measured on the oracle alone at
-    the 175B shape (rows of rms ~ 23): moving 1% of a decode token's elements
-    by one fp16 ulp moves outputs by up to 0.0625 (2.8e-3 rms), and one-ulp
-    moves of 0.1% of a prefill's Q/K/V by up to 0.035.  Near-zero elements of
-    such rows cannot meet 2e-2 absolute; the floor admits 5e-3 rms."""
-    g = np.asarray(gpu, np.float64)
-    r = np.asarray(ref, np.float64)
-    assert g.shape == r.shape, (g.shape, r.shape)
-    assert np.isfinite(g).all(), f"{what}: non-finite GPU values"
-    rms = np.sqrt((r * r).mean(axis=-1, keepdims=True))
-    err = np.abs(g - r) / np.maximum(np.maximum(1.0, np.abs(r)), rms / 4)
-    worst = np.unravel_index(np.argmax(err), err.shape)
-    assert err.max() <= tol, \
-        f"{what}: max scaled err {err.max():.3g} at {worst}: gpu {g[worst]} ref {r[worst]}"
-    return float(err.max())
-
-
 def unpack_nibbles(codes):
     """Generic layout bytes -> codes (byte j holds c[2j] | c[2j+1] << 4)."""
     lo = codes & 15
@@ -85,24 +62,15 @@ def unpack_q4_weight(packed, k, n):
     return c
 
 
-def assert_q4_cache_close(orc, g_codes, g_sm, r_codes, r_sm, what="", min_equal=0.99):
-    """int4 cache rows quantised from fp16 K/V that the two sides computed with
-    differently ordered sums.  A value on a code boundary may round to the
-    neighbouring level, so: most code bytes equal, every code within one
-    level, and every dequantised value within the tolerance or, where the
-    code differs, within one scale step of the reference."""
-    eq = (g_codes == r_codes).mean()
-    assert eq >= min_equal, f"{what}: only {eq:.4f} of code bytes equal"
-    gc = unpack_nibbles(g_codes).astype(np.int32)
-    rc = unpack_nibbles(r_codes).astype(np.int32)
+def check_flips(g_codes, r_codes, what, max_rate):
+    """int4 cache rows that the two sides coded from K/V each computed itself (sums in
+    different orders): reports the share of differing 4-bit codes (the flip rate),
+    requires every code within one level and the rate at most max_rate.  Codes coded
+    from the same fp16 rows are compared bit-exactly elsewhere."""
+    gc = unpack_nibbles(np.asarray(g_codes)).astype(np.int32)
+    rc = unpack_nibbles(np.asarray(r_codes)).astype(np.int32)
+    rate = float((gc != rc).mean())
+    print(f"{what}: code flip rate {rate:.3g}")
     assert np.abs(gc - rc).max() <= 1, f"{what}: a code differs by more than one level"
-    gv = orc.dequantize_g64(g_codes, g_sm).astype(np.float64)
-    rv = orc.dequantize_g64(r_codes, r_sm).astype(np.float64)
-    d = g_codes.shape[-1] * 2
-    step = np.repeat(np.abs(g_sm.view(np.float16)[..., 0].astype(np.float64)), 64, axis=-1)
-    step = step.reshape(gv.shape[:-1] + (d,))
-    allowed = TOL * np.maximum(1.0, np.abs(rv)) + np.where(gc != rc, step, 0.0)
-    err = np.abs(gv - rv)
-    worst = np.unravel_index(np.argmax(err - allowed), err.shape)
-    assert (err <= allowed).all(), \
-        f"{what}: dequantised value off at {worst}: gpu {gv[worst]} ref {rv[worst]}"
+    assert rate <= max_rate, f"{what}: flip rate {rate:.3g} > {max_rate}"
+    return rate
