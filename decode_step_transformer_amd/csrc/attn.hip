@@ -22,6 +22,11 @@
 namespace hp {
 
 // ------------------------------------------------------------ KV append
+// One block row of the grid per new token (request r, token i): the token's K
+// and V columns are 2 h1 contiguous halves of its qkv row, i.e. 2 h1 / 64
+// groups; blockIdx.y picks a run of 32 AU groups of them, a lane codes AU
+// groups (loads issued first) and writes each into the head-major cache row
+// of its head.
 struct AppendArgs {
   const _Float16* qkv;
   int b, q, h1, H, D, pos;
@@ -33,36 +38,41 @@ struct AppendArgs {
   uint32_t* vsm;
 };
 
-template <bool Q4>
+constexpr int AU = 4;
+
+template <bool Q4, int D>
 __global__ __launch_bounds__(256) void k_kv_append(AppendArgs a) {
+  constexpr int G = D / 64;  // groups per head row
   const int sub = threadIdx.x & 7;
-  const int G = a.D / 64;
-  const int64_t groups = 2LL * a.b * a.q * a.H * G;
+  const int token = blockIdx.x;  // r * q + i
+  const int r = token / a.q, i = token % a.q;
+  const int HG = a.H * G;        // groups of K (and of V) per token
   const int pos = a.pos + (a.dpos ? *a.dpos : 0);
-  const int64_t stride = (int64_t)gridDim.x * 32;
-  for (int64_t gi = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); gi < groups; gi += stride) {
-    int64_t rest = gi;
-    const int g = (int)(rest % G);
-    rest /= G;
-    const int h = (int)(rest % a.H);
-    rest /= a.H;
-    const int i = (int)(rest % a.q);
-    rest /= a.q;
-    const int r = (int)(rest % a.b);
-    const int which = (int)(rest / a.b);  // 0 = K, 1 = V
-    const _Float16* src =
-        a.qkv + ((int64_t)r * a.q + i) * 3 * a.h1 + (int64_t)(1 + which) * a.h1 + h * a.D + 64 * g;
-    const uint4 raw = *(const uint4*)(src + 8 * sub);
+  const _Float16* src = a.qkv + (int64_t)token * 3 * a.h1 + a.h1;  // K | V of this token
+  const int gg0 = blockIdx.y * (32 * AU) + (threadIdx.x >> 3);
+  uint4 raw[AU];
+#pragma unroll
+  for (int u = 0; u < AU; ++u) {
+    const int gg = gg0 + 32 * u;
+    if (gg < 2 * HG) raw[u] = stream_load16((const uint4*)(src + 64 * gg) + sub);
+  }
+#pragma unroll
+  for (int u = 0; u < AU; ++u) {
+    const int gg = gg0 + 32 * u;
+    if (gg >= 2 * HG) continue;  // the same for the 8 lanes of a group
+    const int which = gg >= HG;  // 0 = K, 1 = V
+    const int hg = gg - which * HG;
+    const int h = hg / G, g = hg % G;
     const int64_t row = ((int64_t)r * a.H + h) * a.cap + pos + i;
     if constexpr (Q4) {
       uint32_t smw;
-      const uint32_t word = quant_group8(raw, smw);
-      uint8_t* dst = (uint8_t*)(which ? a.v : a.k) + row * (a.D / 2) + 32 * g;
+      const uint32_t word = quant_group8(raw[u], smw);
+      uint8_t* dst = (uint8_t*)(which ? a.v : a.k) + row * (D / 2) + 32 * g;
       *(uint32_t*)(dst + 4 * sub) = word;
       if (sub == 0) (which ? a.vsm : a.ksm)[row * G + g] = smw;
     } else {
-      _Float16* dst = (_Float16*)(which ? a.v : a.k) + row * a.D + 64 * g;
-      *(uint4*)(dst + 8 * sub) = raw;
+      _Float16* dst = (_Float16*)(which ? a.v : a.k) + row * D + 64 * g;
+      *(uint4*)(dst + 8 * sub) = raw[u];
     }
   }
 }
@@ -544,14 +554,16 @@ void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const voi
   AppendArgs a{(const _Float16*)qkv, b,  q,        h1,   heads,
                h1 / heads,          pos, dpos,     kv.cap, kv.k,
                kv.v,                (uint32_t*)kv.k_sm, (uint32_t*)kv.v_sm};
-  const int64_t groups = 2LL * b * q * heads * ((h1 / heads) / 64);
-  if (groups == 0) return;
-  const int blocks = (int)std::min<int64_t>(cdiv(groups, 32), 16384);
+  const int64_t tokens = (int64_t)b * q;
+  if (tokens == 0) return;
+  const dim3 grid((unsigned)tokens, (unsigned)cdiv(2 * (h1 / 64), 32 * AU));
   Prof prof(kv.fmt == HP_Q4 ? "kv_append_q4" : "kv_append_f16", st);
+  const int D = h1 / heads;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a); };
   if (kv.fmt == HP_Q4)
-    hipLaunchKernelGGL(k_kv_append<true>, dim3(blocks), dim3(256), 0, st, a);
+    D == 128 ? go(k_kv_append<true, 128>) : go(k_kv_append<true, 64>);
   else
-    hipLaunchKernelGGL(k_kv_append<false>, dim3(blocks), dim3(256), 0, st, a);
+    D == 128 ? go(k_kv_append<false, 128>) : go(k_kv_append<false, 64>);
 }
 
 void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,

@@ -11,16 +11,32 @@
 
 namespace hp {
 
+// Each lane codes QU groups whose loads are all issued before the first is
+// used: with one 16-byte load per lane in flight, even a full CU (32 waves)
+// holds only 32 KB of requests, too few to cover HBM latency.
+constexpr int QU = 4;
+
 __global__ __launch_bounds__(256) void k_quantize_g64(const uint4* __restrict__ x, int64_t groups,
                                                       uint32_t* __restrict__ codes,
                                                       uint32_t* __restrict__ sm) {
   const int sub = threadIdx.x & 7;
-  const int64_t stride = (int64_t)gridDim.x * 32;
-  for (int64_t g = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); g < groups; g += stride) {
-    uint32_t smw;
-    const uint32_t word = quant_group8(x[g * 8 + sub], smw);
-    codes[g * 8 + sub] = word;
-    if (sub == 0) sm[g] = smw;
+  // block: QU runs of 32 groups; wave w takes groups 8 w .. 8 w + 7 of each run
+  const int64_t g0 = (int64_t)blockIdx.x * (32 * QU) + (threadIdx.x >> 3);
+  uint4 raw[QU];
+#pragma unroll
+  for (int u = 0; u < QU; ++u) {
+    const int64_t g = g0 + 32 * u;
+    if (g < groups) raw[u] = stream_load16(x + g * 8 + sub);
+  }
+#pragma unroll
+  for (int u = 0; u < QU; ++u) {
+    const int64_t g = g0 + 32 * u;
+    if (g < groups) {  // the same for the 8 lanes of a group
+      uint32_t smw;
+      const uint32_t word = quant_group8(raw[u], smw);
+      codes[g * 8 + sub] = word;
+      if (sub == 0) sm[g] = smw;
+    }
   }
 }
 
@@ -114,7 +130,7 @@ void launch_quantize_g64(const void* x, int64_t rows, int64_t cols, void* codes,
   const int64_t groups = rows * (cols / 64);
   if (groups == 0) return;
   Prof prof("quantize_g64", st);
-  hipLaunchKernelGGL(k_quantize_g64, dim3(grid_for(groups, 32)), dim3(256), 0, st,
+  hipLaunchKernelGGL(k_quantize_g64, dim3((unsigned)cdiv(groups, 32 * QU)), dim3(256), 0, st,
                      (const uint4*)x, groups, (uint32_t*)codes, (uint32_t*)sm);
 }
 

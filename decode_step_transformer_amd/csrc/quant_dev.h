@@ -25,6 +25,14 @@ __device__ __forceinline__ uint32_t f16_bits_of(float x) {
 // 2^-15 from a half-integer, rint(t') = rint(t).  Only the rare elements
 // near a rounding boundary (and NaN, or infinite inputs) take the exact
 // division; the result is bit-identical to evaluating t for every element.
+// 16-byte load of data read once (non-temporal: it should not displace
+// reusable lines in the caches).
+__device__ __forceinline__ uint4 stream_load16(const uint4* p) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  const v4 v = __builtin_nontemporal_load((const v4*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float quant_dpp(float v) {
   return __builtin_bit_cast(
