@@ -55,6 +55,16 @@ size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt);
 hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, const void* res,
                       int64_t ldr, bool relu, void* y, int64_t ldy, void* ws, hipStream_t st);
 
+// Largest M run as a skinny product (one row tile, split k); taller products
+// run on the tiled kernel.
+constexpr int64_t kSkinnyM = 144;
+// Size of the static scratch behind hp_gemm_noalloc (split-k partials of
+// skinny products: 63.7 MB at the largest, the 175B QKV product at M = 144).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+// Device address of that scratch on the current device (looked up once per
+// device with hipGetSymbolAddress).
+hp_status static_scratch(void** ptr);
+
 // Skinny int4 product (1 <= M <= 144) on the 8-wave decode kernel; with
 // splits > 1 the k-range is split, fp32 partials go to `partials` (the
 // kernel's tile-major layout, gemm_ws_bytes of them) and a second kernel adds

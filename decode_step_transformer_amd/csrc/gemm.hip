@@ -24,6 +24,7 @@
 //    order, so the result depends only on (k, n), never on M.  Skinny int4
 //    products run on the 8-wave kernel of gemm_dec.hip (same split rule);
 //    tall ones expand int4 weights to fp16 and run k_gemm16.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -33,7 +34,7 @@ namespace hp {
 
 constexpr int BK = 128;        // k-block (one packed q4 tile in depth)
 constexpr int LDS_ROW = 136;   // halves per staged activation row (128 + 8 pad)
-constexpr int SKINNY_M = 144;  // largest M handled as one row tile with split-k
+constexpr int SKINNY_M = (int)kSkinnyM;  // largest M handled as one row tile with split-k
 
 
 // Calls f(integral_constant<0>) .. f(integral_constant<N-1>): compile-time
@@ -365,6 +366,33 @@ size_t gemm_ws_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {
   }
   const int s = split_for(k, n);
   return s > 1 ? (size_t)s * (size_t)M * (size_t)n * sizeof(float) : 0;
+}
+
+// ------------------------------------------------ allocation-free scratch
+// Split-k partial sums for hp_gemm_noalloc: a fixed array in the code
+// object, one copy per GPU, resident until the process ends.  In host code
+// `scratch` names a host-side stand-in, never a device address: kernels get
+// the address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[64];
+
+hp_status static_scratch(void** ptr) {
+  int dev = -1;
+  hp_status s = hip_ok(hipGetDevice(&dev), "hipGetDevice");
+  if (s != HP_OK) return s;
+  if (dev < 0 || dev >= 64) return fail(HP_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if ((s = hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress")) != HP_OK)
+      return s;
+    if (!p) return fail(HP_ERR_HIP, "hipGetSymbolAddress returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return HP_OK;
 }
 
 template <int TM>

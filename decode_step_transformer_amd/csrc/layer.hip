@@ -415,6 +415,33 @@ hp_status hp_gemm(const void* x, int64_t ldx, const hp_mat* w, int64_t M, const 
   return launch_gemm(x, ldx, *w, M, res, ldr, relu != 0, y, ldy, ws, S(stream));
 }
 
+hp_status hp_gemm_noalloc(const void* x, int64_t ldx, const hp_mat* w, int64_t M,
+                          const void* res, int64_t ldr, int32_t relu, void* y, int64_t ldy,
+                          void* stream) {
+  if (!w) return fail(HP_ERR_NULL, "w is NULL");
+  if (M < 0) return fail(HP_ERR_SHAPE, "M < 0");
+  hp_status s = check_mat(*w, w->k, w->n, "w");
+  if (s != HP_OK) return s;
+  if (M == 0) return HP_OK;
+  if (M > kSkinnyM)
+    return fail(HP_ERR_SHAPE, "hp_gemm_noalloc takes M <= %d rows (M = %lld); taller products "
+                "need a weight-sized buffer: use hp_gemm", (int)kSkinnyM, (long long)M);
+  if (!x || !y) return fail(HP_ERR_NULL, "NULL pointer");
+  NEED_ALIGN(x, 16);
+  NEED_ALIGN(y, 8);
+  if (res) NEED_ALIGN(res, 8);
+  if (ldx < w->k || ldx % 8 || ldy < w->n || ldy % 4 || (res && (ldr < w->n || ldr % 4)))
+    return fail(HP_ERR_SHAPE, "row strides too small or misaligned");
+  const size_t need = gemm_ws_bytes(M, w->k, w->n, w->fmt);
+  if (need > kStaticScratchBytes)
+    return fail(HP_ERR_WORKSPACE, "product needs %zu bytes of split partials, above the %zu-byte "
+                "static scratch", need, kStaticScratchBytes);
+  if ((s = device_check()) != HP_OK) return s;
+  void* ws = nullptr;
+  if ((s = static_scratch(&ws)) != HP_OK) return s;
+  return launch_gemm(x, ldx, *w, M, res, ldr, relu != 0, y, ldy, ws, S(stream));
+}
+
 hp_status hp_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
                        int32_t pos, const hp_kv* kv, void* stream) {
   if (b <= 0 || q <= 0 || h1 <= 0 || heads <= 0 || h1 % heads || pos < 0)

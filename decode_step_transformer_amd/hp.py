@@ -52,6 +52,7 @@ class hp_dims(C.Structure):
 EXPORTS = [
     "hp_last_error", "hp_device_check", "hp_quantize_g64", "hp_dequantize_g64",
     "hp_pack_weight_q4", "hp_pack_weight_f16", "hp_gemm_workspace_bytes", "hp_gemm",
+    "hp_gemm_noalloc",
     "hp_kv_append", "hp_prefill_attention", "hp_decode_attention", "hp_decode_attention_ragged",
     "hp_topk_attention",
     "hp_tree_masks",
@@ -80,6 +81,7 @@ def lib():
             "hp_pack_weight_q4": [_p, _p, _i32, _i32, _p, _p, _p, _p],
             "hp_pack_weight_f16": [_p, _i32, _i32, _p, _p],
             "hp_gemm": [_p, _i64, C.POINTER(hp_mat), _i64, _p, _i64, _i32, _p, _i64, _p, _sz, _p],
+            "hp_gemm_noalloc": [_p, _i64, C.POINTER(hp_mat), _i64, _p, _i64, _i32, _p, _i64, _p],
             "hp_kv_append": [_i32, _i32, _i32, _i32, _p, _i32, C.POINTER(hp_kv), _p],
             "hp_prefill_attention": [_i32, _i32, _i32, _i32, _p, _p, _p],
             "hp_decode_attention": [_i32, _i32, _i32, _i32, _p, _i32, _p, C.POINTER(hp_kv), _p, _p],
@@ -225,6 +227,17 @@ def hp_gemm(x: torch.Tensor, w: Mat, res=None, relu=False, out=None, ws=None, st
     _check(lib().hp_gemm(_ptr(x), x.stride(0), C.byref(mc), M, _ptr(res),
                          res.stride(0) if res is not None else 0, int(relu), _ptr(y), y.stride(0),
                          _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+    return y
+
+
+def hp_gemm_noalloc(x: torch.Tensor, w: Mat, res=None, relu=False, out=None, stream=None):
+    """hp_gemm without a workspace: split partials go to the library's static scratch."""
+    M = x.shape[0]
+    y = out if out is not None else torch.empty((M, w.n), dtype=torch.float16, device=x.device)
+    mc = w.c()
+    _check(lib().hp_gemm_noalloc(_ptr(x), x.stride(0), C.byref(mc), M, _ptr(res),
+                                 res.stride(0) if res is not None else 0, int(relu), _ptr(y),
+                                 y.stride(0), _stream(stream)))
     return y
 
 

@@ -166,6 +166,22 @@ hp_status hp_gemm(const void* x, int64_t ldx, const hp_mat* w, int64_t M, const 
                   int64_t ldr, int32_t relu, void* y, int64_t ldy, void* ws, size_t ws_bytes,
                   void* stream);
 
+/* hp_gemm for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same product, kernels and results as hp_gemm
+ * (bit for bit), with the split-k partial sums in a static device array of
+ * 64 MiB that the library holds on each GPU it runs on until the process
+ * ends.  Nothing is allocated.  Takes 1 <= M <= 144 rows (the decode-step
+ * products; M = 0 is a no-op); a taller M, or a product whose partials need
+ * more than 64 MiB (hp_gemm_workspace_bytes), returns HP_ERR_SHAPE or
+ * HP_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap on a GPU (concurrent streams or
+ * host threads) race and must be serialised by the caller; each call
+ * overwrites every partial it reads, so nothing needs clearing. */
+hp_status hp_gemm_noalloc(const void* x, int64_t ldx, const hp_mat* w, int64_t M,
+                          const void* res, int64_t ldr, int32_t relu, void* y, int64_t ldy,
+                          void* stream);
+
 /* [FlexGen] decode equations (Concat) and section 5 (KV grouped along the
  * hidden dimension): for each request r < b and new token i < q, copies (or
  * quantises) the K and V rows of token i into cache rows pos + i.

@@ -75,3 +75,22 @@ def test_gemm_host_checks():
     nul = hp.hp_mat(hp.HP_Q4, 256, 512, fake, None, fake)               # no scales
     assert L.hp_gemm(None, 256, C.byref(nul), 4, None, 0, 0, None, 512, None, 0, None) == -1
     assert L.hp_gemm(None, 256, None, 4, None, 0, 0, None, 512, None, 0, None) == -1
+
+
+def test_gemm_noalloc_host_checks():
+    """hp_gemm_noalloc refuses, on the host and before any device call, a product
+    taller than the skinny limit (M > 144 needs a weight-sized buffer) and one whose
+    split partials exceed its 64 MiB static scratch (k = 49152, n = 24576 at M = 144
+    needs 67.5 MiB); M = 0 is a no-op.  The pointers are never dereferenced."""
+    import ctypes as C
+    from decode_step_transformer_amd import hp
+    L = hp.lib()
+    fake = 0x100000
+    m = hp.hp_mat(hp.HP_Q4, 256, 512, fake, fake, fake)
+    assert L.hp_gemm_noalloc(None, 256, C.byref(m), 0, None, 0, 0, None, 512, None) == 0
+    assert L.hp_gemm_noalloc(fake, 256, C.byref(m), 145, None, 0, 0, fake, 512, None) == -2
+    assert "M <= 144" in hp.hp_last_error()
+    big = hp.hp_mat(hp.HP_Q4, 49152, 24576, fake, fake, fake)
+    assert hp.hp_gemm_workspace_bytes(144, 49152, 24576, hp.HP_Q4) > 64 << 20
+    assert L.hp_gemm_noalloc(fake, 49152, C.byref(big), 144, None, 0, 0, fake, 24576, None) == -5
+    assert "static scratch" in hp.hp_last_error()
