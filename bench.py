@@ -302,6 +302,52 @@ def tiny_block(hp, torch, stream, reps=5):
     return res
 
 
+def other_config_block(hp, torch, stream, name):
+    """One more configuration's whole block (prefill column + n graph-replayed decode
+    columns over every layer): one warm-up block, then one timed block with the
+    per-kernel event times of hp_profile, and the decode column again on finite data
+    (refill_finite, decode_column_finite).  Its tensors are freed on return."""
+    c = CONFIGS[name]
+    hp.hp_release_graphs()
+    d, layers, x, t_in, kvs, ws, x_out, t_out = setup(c, CONFIG_SEED[name], hp, torch)
+    b, n, s, l = c["b"], c["n"], c["s"], c["l"]
+    hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws, hp.HP_GRAPH, timing=True,
+                    stream=stream)
+    hp.hp_profile(True)
+    pre, dec = hp.hp_run_block(d, layers, x, t_in, kvs, x_out, t_out, ws, hp.HP_GRAPH,
+                               timing=True, stream=stream)
+    hp.hp_profile(False)
+    prof = hp.hp_profile_read()
+    nonfinite = int((~torch.isfinite(t_out.float())).sum().item())
+    refill_finite(hp, torch, stream, c, kvs)
+    dcol = decode_column_finite(hp, torch, stream, c, d, layers, kvs, ws)
+    out = {"config": {"workload": f"{name} block", "l": l, "h1": c["h1"], "h2": c["h2"],
+                      "heads": c["heads"], "b": b, "gbs": c["gbs"], "s": s, "n": n,
+                      "weights": "int4-g64" if c["fmt"] else "fp16",
+                      "kv": "int4-g64" if c["fmt"] else "fp16"},
+           "tokens_per_s": b * n / (dec / 1e3), "prefill_ms": pre, "decode_ms": dec,
+           "tokens_per_s_incl_prefill": b * n / ((pre + dec) / 1e3),
+           "nonfinite_decode_outputs": nonfinite,
+           "decode_column_finite": dict(dcol, block_column_ms=dec / n),
+           "resident_GB": {"weights": sum(ly.nbytes() for ly in layers) / 1e9,
+                           "kv": sum(kv.nbytes() for kv in kvs) / 1e9}}
+    cnt, tot = prof.get("gemm_f16_tiled", (0, 0.0))
+    if cnt:
+        achieved = l * layer_flops(c, b * s) / 1e12 / (tot / 1e3)
+        out["prefill_gemm"] = {"kernel": "gemm_f16_tiled", "avg_launch_ms": tot / cnt,
+                               "tflops": achieved, "frac_mfma": achieved / MFMA_F16_PEAK_TFLOPS}
+    out["kernels"] = {k: {"launches": v[0], "total_ms": v[1]} for k, v in prof.items()}
+    if name == "opt-175b-int4":
+        # [FlexGen] evaluation: 1.12 tokens/s for this workload including prefill on one
+        # T4 with CPU and SSD offloading -- context, not a target
+        out["page_reference"] = {"tokens_per_s_incl_prefill": 1.12,
+                                 "hardware": "1x T4 16 GB + CPU DRAM + SSD offload"}
+    del d, layers, x, t_in, kvs, ws, x_out, t_out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_products(hp, torch, stream, c, layers):
     """The four decode-phase products of a layer at M = b ([FlexGen] background
     section: x·w_QKV, ·w_O + residual, relu(·w_1), ·w_2 + residual), each run once per
@@ -509,6 +555,8 @@ def main():
     ap.add_argument("--no-tree", action="store_true", help="skip the tree-attention workload")
     ap.add_argument("--no-topk-block", action="store_true",
                     help="skip the extra block with Top-K sparse decode attention")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the one-block runs of the other OPT configurations")
     ap.add_argument("--no-diagonal", action="store_true",
                     help="skip the extra run of the block under the diagonal schedule")
     args = ap.parse_args()
@@ -617,6 +665,17 @@ def main():
         tree = None if args.no_tree else tree_attention(hp, torch, stream)
         log("tiny block")
         tiny = tiny_block(hp, torch, stream)
+        others = {}
+        if not args.no_other_configs:
+            # the other OPT shapes, one block each (the timed block's buffers freed
+            # first: the 175B weights and cache take 202 GB)
+            del layers, kvs, ws, x, t_in, x_out, t_out
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            for oname in ("opt-6.7b-fp16", "opt-175b-int4"):
+                if oname != args.config:
+                    log(f"other configuration: {oname}")
+                    others[oname] = other_config_block(hp, torch, stream, oname)
 
     b, n, s, l = c["b"], c["n"], c["s"], c["l"]
     K = args.steps
@@ -709,6 +768,7 @@ def main():
         "quant_kernels": qk,
         "prefill_gemm_finite": dict(pgemm, block_avg_launch_ms=roof.get("avg_launch_ms")),
         "tiny_block": tiny,
+        "other_configs": others or None,
         "topk10_block": topk_block,
         "diagonal_block": None if diag is None else dict(
             diag, tokens_per_s_incl_prefill=b * n / (diag["total_ms"] / 1e3),
