@@ -31,12 +31,24 @@ struct AppendArgs {
   const _Float16* qkv;
   int b, q, h1, H, D, pos;
   const int32_t* dpos;
+  const int32_t* rpos;  // per-request first row (clamped to [0, pos]), or NULL
   int cap;
   void* k;
   void* v;
   uint32_t* ksm;
   uint32_t* vsm;
+  const int32_t* pages;  // paged cache: page table [b][cap / PR], or NULL
+  int PR, pool;          // rows per page, pages in the pool
 };
+
+// Physical cache row (in rows of one head) of logical row j of request r,
+// head h: contiguous [b][H][cap], or paged [page][H][PR] through the table.
+__device__ __forceinline__ int64_t cache_row(const int32_t* pages, int PR, int pool, int cap,
+                                             int H, int r, int h, int j) {
+  if (!pages) return ((int64_t)r * H + h) * cap + j;
+  const int pg = min(max(pages[(int64_t)r * (cap / PR) + j / PR], 0), pool - 1);
+  return ((int64_t)pg * H + h) * PR + j % PR;
+}
 
 constexpr int AU = 4;
 
@@ -47,7 +59,7 @@ __global__ __launch_bounds__(256) void k_kv_append(AppendArgs a) {
   const int token = blockIdx.x;  // r * q + i
   const int r = token / a.q, i = token % a.q;
   const int HG = a.H * G;        // groups of K (and of V) per token
-  const int pos = a.pos + (a.dpos ? *a.dpos : 0);
+  const int pos = a.rpos ? min(max(a.rpos[r], 0), a.pos) : a.pos + (a.dpos ? *a.dpos : 0);
   const _Float16* src = a.qkv + (int64_t)token * 3 * a.h1 + a.h1;  // K | V of this token
   const int gg0 = blockIdx.y * (32 * AU) + (threadIdx.x >> 3);
   uint4 raw[AU];
@@ -63,7 +75,7 @@ __global__ __launch_bounds__(256) void k_kv_append(AppendArgs a) {
     const int which = gg >= HG;  // 0 = K, 1 = V
     const int hg = gg - which * HG;
     const int h = hg / G, g = hg % G;
-    const int64_t row = ((int64_t)r * a.H + h) * a.cap + pos + i;
+    const int64_t row = cache_row(a.pages, a.PR, a.pool, a.cap, a.H, r, h, pos + i);
     if constexpr (Q4) {
       uint32_t smw;
       const uint32_t word = quant_group8(raw[u], smw);
@@ -90,6 +102,8 @@ struct DecArgs {
   const uint32_t* ksm;
   const uint32_t* vsm;
   _Float16* out;
+  const int32_t* pages;  // paged cache (streaming kernel only), or NULL
+  int PR, pool;
 };
 // Cache rows before the new tokens of request r: the same for every request
 // (pos, plus the step counter of a replayed graph), or per request.
@@ -113,12 +127,16 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   const int P = prefix_len(a, r);
   const int R = MASKED ? P + a.q : P + i + 1;
   const uint64_t mask = MASKED ? a.masks[(int64_t)r * a.q + i] : 0ull;
-  // wave-uniform bases, per-lane 32-bit byte offsets
+  // wave-uniform bases, per-lane 32-bit byte offsets.  The rows of a chunk
+  // (CR rows, CR | 64 | PR) lie in one page of a paged cache: base(c) is the
+  // physical row of logical row 0 of that chunk's page, less that page's
+  // first logical row, so logical row j of the chunk is at base(c) + j.
   const int64_t rowbase = ((int64_t)r * a.H + h) * a.cap;
-  const uint8_t* kb = (const uint8_t*)a.k + rowbase * RB;
-  const uint8_t* vb = (const uint8_t*)a.v + rowbase * RB;
-  const uint8_t* ksb = (const uint8_t*)(a.ksm + rowbase * G);
-  const uint8_t* vsb = (const uint8_t*)(a.vsm + rowbase * G);
+  auto base = [&](int c) __attribute__((always_inline)) -> int64_t {
+    if (!a.pages) return rowbase;
+    const int j = min(c * CR, R - 1);
+    return cache_row(a.pages, a.PR, a.pool, a.cap, a.H, r, h, j) - j;
+  };
   const int g = Q4 ? (32 * qd) / 64 : 0;  // int4 group of this lane's dims
   const uint32_t lane_off = 16 * qd, lane_soff = 4 * g;
   // exp(x / sqrt(D)) = exp2(x * c2)
@@ -131,7 +149,10 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   float m_run = -INFINITY, l_lane = 0.f;
 
   // rows past the visible range are clamped to its last row (their weight is 0)
-  auto load = [&](DecPart<U, Q4>& X, const uint8_t* cb, const uint8_t* sb, int c) {
+  auto load = [&](DecPart<U, Q4>& X, const void* cache, const uint32_t* smc, int c) {
+    const int64_t b0 = base(c);
+    const uint8_t* cb = (const uint8_t*)cache + b0 * RB;
+    const uint8_t* sb = (const uint8_t*)(smc + b0 * G);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t row = (uint32_t)min(c * CR + rho + RPI * u, R - 1);
@@ -151,8 +172,8 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   // other phase computes.
   DecPart<U, Q4> K, V;
   const int nc = (R + CR - 1) / CR;
-  load(K, kb, ksb, 0);
-  load(V, vb, vsb, 0);
+  load(K, a.k, a.ksm, 0);
+  load(V, a.v, a.vsm, 0);
   for (int c = 0; c < nc; ++c) {
     float s[U];
 #pragma unroll
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
         valid = valid & ((row < P) | (bool)((mask >> ((unsigned)(row - P) & 63u)) & 1ull));
       s[u] = valid ? t : -INFINITY;
     }
-    load(K, kb, ksb, c + 1);
+    load(K, a.k, a.ksm, c + 1);
     // online softmax (chunk max is wave-uniform)
     float cm = s[0];
 #pragma unroll
@@ -184,7 +205,7 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
     l_lane = fmaf(l_lane, alpha, ps);
     if (alpha != 1.f) A.rescale(alpha);
     A.add(V, p, dq);
-    load(V, vb, vsb, c + 1);
+    load(V, a.v, a.vsm, c + 1);
   }
   A.finish(l_lane, rho, a.out + ((int64_t)r * a.q + i) * a.h1 + h * D + (Q4 ? 32 : 8) * qd);
 }
@@ -550,10 +571,12 @@ __global__ __launch_bounds__(256, 2) void k_multi_attn(DecArgs a) {
 
 // -------------------------------------------------------------- launchers
 void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
-                      int32_t pos, const int32_t* dpos, const hp_kv& kv, hipStream_t st) {
-  AppendArgs a{(const _Float16*)qkv, b,  q,        h1,   heads,
-               h1 / heads,          pos, dpos,     kv.cap, kv.k,
-               kv.v,                (uint32_t*)kv.k_sm, (uint32_t*)kv.v_sm};
+                      int32_t pos, const int32_t* dpos, const int32_t* rpos, const hp_kv& kv,
+                      hipStream_t st) {
+  AppendArgs a{(const _Float16*)qkv, b,    q,       h1,     heads,
+               h1 / heads,          pos,  dpos,    rpos,   kv.cap,
+               kv.k,                kv.v, (uint32_t*)kv.k_sm, (uint32_t*)kv.v_sm,
+               kv.page_rows > 0 ? kv.pages : nullptr, kv.page_rows, kv.pool_pages};
   const int64_t tokens = (int64_t)b * q;
   if (tokens == 0) return;
   const dim3 grid((unsigned)tokens, (unsigned)cdiv(2 * (h1 / 64), 32 * AU));
@@ -571,7 +594,8 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
                              const uint64_t* masks, const hp_kv& kv, void* out, hipStream_t st) {
   DecArgs a{(const _Float16*)qkv, q,      h1,   heads, pos,  dpos,
             plen,                 masks,  kv.cap, kv.k, kv.v, (const uint32_t*)kv.k_sm,
-            (const uint32_t*)kv.v_sm, (_Float16*)out};
+            (const uint32_t*)kv.v_sm, (_Float16*)out,
+            kv.page_rows > 0 ? kv.pages : nullptr, kv.page_rows, kv.pool_pages};
   const int D = h1 / heads;
   if (kv.fmt == HP_Q4 && q >= 16) {
     Prof prof("attn_multi_q4", st);

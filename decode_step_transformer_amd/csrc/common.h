@@ -91,8 +91,12 @@ inline int64_t pad_ld(int64_t n) { return n % 8192 == 0 ? n + 64 : n; }
 // KV append / attention.  `dpos` (device int32, may be NULL): when set, the
 // kernels read pos from it (plus pos as an offset), so a captured graph can
 // be replayed at advancing positions.
+// rpos (device int32 [b], may be NULL): per-request first rows, each clamped
+// to [0, pos]; then dpos is ignored.  Paged caches (kv.page_rows > 0) go
+// through kv.pages.
 void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
-                      int32_t pos, const int32_t* dpos, const hp_kv& kv, hipStream_t st);
+                      int32_t pos, const int32_t* dpos, const int32_t* rpos, const hp_kv& kv,
+                      hipStream_t st);
 void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, const void* qkv,
                               void* out, hipStream_t st);
 // plen (device int32 [b], may be NULL): per-request prefix lengths, each

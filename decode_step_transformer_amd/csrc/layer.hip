@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <set>
 #include <string>
 #include <vector>
 
@@ -70,6 +71,90 @@ static void launch_set_i32(int32_t* p, int32_t v, bool add, hipStream_t st) {
 
 void launch_add_i32(int32_t* p, int32_t v, hipStream_t st) { launch_set_i32(p, v, true, st); }
 
+// Diagonal schedule ([FlexGen] appendix A.2): the live requests r0 .. r0 + M
+// of iteration it, request r in GPU batch r / gbs at decode step
+// t = it - r / gbs.  direction 0: dst row i = t_in[t - 1][r] and rpos[i] =
+// s + t - 1 (the row of its new token); direction 1: t_out[t - 1][r] = src
+// row i.  Rows of h1 halves, 16-byte units.
+__global__ __launch_bounds__(256) void k_diag_rows(const uint4* __restrict__ src,
+                                                   uint4* __restrict__ dst,
+                                                   int32_t* __restrict__ rpos, int M, int r0,
+                                                   int gbs, int b, int s, int it, int h1,
+                                                   int direction) {
+  const int w = h1 / 8;  // 16-byte units per row
+  const int64_t total = (int64_t)M * w;
+  const int64_t gs = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gs) {
+    const int i = (int)(e / w), c = (int)(e % w);
+    const int r = r0 + i, t = it - r / gbs;
+    const int64_t step_row = ((int64_t)(t - 1) * b + r) * w + c;
+    if (direction == 0) {
+      dst[(int64_t)i * w + c] = src[step_row];
+      if (c == 0) rpos[i] = s + t - 1;
+    } else {
+      dst[step_row] = src[(int64_t)i * w + c];
+    }
+  }
+}
+
+static void launch_diag_rows(const void* src, void* dst, int32_t* rpos, int M, int r0, int gbs,
+                             int b, int s, int it, int h1, int direction, hipStream_t st) {
+  const int64_t units = (int64_t)M * (h1 / 8);
+  const int blocks = (int)std::min<int64_t>(cdiv(units, 256), 4096);
+  Prof prof("diag_rows", st);
+  hipLaunchKernelGGL(k_diag_rows, dim3(blocks), dim3(256), 0, st, (const uint4*)src, (uint4*)dst,
+                     rpos, M, r0, gbs, b, s, it, h1, direction);
+}
+
+// [FlexGen] appendix A.2 (diagonal block schedule): the cache pages of
+// page_rows rows that each request holds, when every live request keeps
+// only the pages its current length needs.  Request r of GPU batch k takes
+// the pages of rows [0, s) at its prefill (iteration k) and, at decode step t
+// (iteration k + t), those of rows up to s + t; after its last step (t = n)
+// its batch's pages return to the pool.  Free pages go out lowest index
+// first.  Fills table [b][cap / page_rows] (-1: never used) if given and
+// returns the peak count of pages in use.
+static int64_t diag_page_plan(const hp_dims& d, int page_rows, int cap,
+                              std::vector<int32_t>* table) {
+  const int nb = d.b / d.gbs, ppr = cap / page_rows;
+  std::vector<int32_t> tb((size_t)d.b * ppr, -1);
+  std::vector<int> held((size_t)d.b, 0);
+  std::set<int32_t> free_pages;
+  int32_t next = 0;
+  int64_t used = 0, peak = 0;
+  auto grow = [&](int k, int rows) {
+    const int need = (int)cdiv(rows, page_rows);
+    for (int i = 0; i < d.gbs; ++i) {
+      const int64_t r = (int64_t)k * d.gbs + i;
+      for (; held[r] < need; ++held[r], ++used) {
+        int32_t p = next;
+        if (!free_pages.empty()) {
+          p = *free_pages.begin();
+          free_pages.erase(free_pages.begin());
+        } else {
+          ++next;
+        }
+        tb[(size_t)r * ppr + held[r]] = p;
+      }
+    }
+  };
+  for (int it = 0; it < nb + d.n; ++it) {
+    if (it < nb) grow(it, d.s);
+    for (int k = std::max(0, it - d.n); k <= std::min(it - 1, nb - 1); ++k) grow(k, d.s + (it - k));
+    peak = std::max(peak, used);
+    const int k = it - d.n;  // batch whose last decode step was this iteration
+    if (k >= 0 && k < nb) {
+      for (int i = 0; i < d.gbs; ++i) {
+        const int64_t r = (int64_t)k * d.gbs + i;
+        for (int pg = 0; pg < held[r]; ++pg) free_pages.insert(tb[(size_t)r * ppr + pg]);
+        used -= held[r];
+      }
+    }
+  }
+  if (table) table->swap(tb);
+  return peak;
+}
+
 // ---------------------------------------------------------------- checks
 static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 #define NEED_ALIGN(p, a)                                                              \
@@ -127,7 +212,14 @@ static hp_status check_layer(const hp_layer& w, int h1, int h2) {
   return HP_OK;
 }
 
-static hp_status check_kv(const hp_kv* kv, int need_rows) {
+// Decode attention with q new tokens runs on the streaming kernel (which
+// reads paged caches) unless the cache is int4 and q >= 16 (multi-query MFMA
+// kernel).
+static bool streaming_attention(const hp_kv* kv, int q) { return kv->fmt != HP_Q4 || q < 16; }
+
+// paged: 0 = contiguous caches only; 1 = paged caches with a page table
+// also accepted; 2 = a page pool whose table the library fills (pages NULL).
+static hp_status check_kv(const hp_kv* kv, int need_rows, int paged = 0) {
   if (!kv) return fail(HP_ERR_NULL, "kv is NULL");
   if (kv->fmt != HP_F16 && kv->fmt != HP_Q4) return fail(HP_ERR_SHAPE, "kv: bad format");
   if (!kv->k || !kv->v) return fail(HP_ERR_NULL, "kv: k/v NULL");
@@ -137,12 +229,24 @@ static hp_status check_kv(const hp_kv* kv, int need_rows) {
     return fail(HP_ERR_SHAPE, "kv: buffers must be 16-byte aligned (sm 4-byte)");
   if (kv->cap <= 0 || need_rows > kv->cap)
     return fail(HP_ERR_CAPACITY, "kv: %d rows needed, cap %d", need_rows, kv->cap);
+  if (kv->page_rows == 0) {
+    if (kv->pages || kv->pool_pages) return fail(HP_ERR_SHAPE, "kv: pages set with page_rows 0");
+    return HP_OK;
+  }
+  if (paged == 0) return fail(HP_ERR_SHAPE, "kv: this call takes contiguous caches only");
+  if (kv->page_rows < 0 || kv->page_rows % 64 || kv->cap % kv->page_rows || kv->pool_pages <= 0)
+    return fail(HP_ERR_SHAPE, "kv: page_rows must be a positive multiple of 64 dividing cap, "
+                "pool_pages positive (page_rows %d, cap %d, pool %d)", kv->page_rows, kv->cap,
+                kv->pool_pages);
+  if (paged == 1 && !kv->pages) return fail(HP_ERR_NULL, "kv: paged cache without a page table");
+  if (paged == 2 && kv->pages) return fail(HP_ERR_SHAPE, "kv: the page table of a pool is the library's");
+  if (paged == 1) NEED_ALIGN(kv->pages, 4);
   return HP_OK;
 }
 
 // ---------------------------------------------------------------- workspace
 struct Ws {
-  size_t qkv, a, xo, hid, part, xb, t0, t1, ctr, total;
+  size_t qkv, a, xo, hid, part, xb, t0, t1, ctr, pt, rpos, total;
 };
 
 static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -171,6 +275,10 @@ static Ws ws_layout(const hp_dims& d) {
   w.t0 = o;  o += al(Md * d.h1 * 2);
   w.t1 = o;  o += al(Md * d.h1 * 2);
   w.ctr = o; o += 256;
+  // diagonal schedule with paged caches: page table [b][ceil((s + n) / 64)]
+  // (pages of at least 64 rows) and one row position per request
+  w.pt = o;  o += al((size_t)d.b * cdiv(d.s + d.n, 64) * 4);
+  w.rpos = o; o += al((size_t)d.b * 4);
   w.total = o;
   return w;
 }
@@ -204,7 +312,7 @@ static hp_status prefill_body(int b, int s, int h1, int h2, int heads, const hp_
   if ((r = launch_gemm(x, h1, w.wqkv, M, nullptr, 0, false, qkv, 3 * h1, at<void>(ws, L.part), st)) !=
       HP_OK)
     return r;
-  launch_kv_append(b, s, h1, heads, qkv, 0, nullptr, kv, st);
+  launch_kv_append(b, s, h1, heads, qkv, 0, nullptr, nullptr, kv, st);
   if ((r = launch_ok("k_kv_append")) != HP_OK) return r;
   launch_prefill_attention(b, s, h1, heads, qkv, at<void>(ws, L.a), st);
   if ((r = launch_ok("k_prefill_attn")) != HP_OK) return r;
@@ -213,17 +321,19 @@ static hp_status prefill_body(int b, int s, int h1, int h2, int heads, const hp_
 
 // topk_max_t > 0: Top-K sparse attention ([FlexGen] section 5) keeping
 // ceil(T / 10) rows, with T <= topk_max_t (q == 1 only).
+// rpos (device int32 [b], may be NULL): each request's own row for its new
+// token (at most pos); the attention then sees that request's rows up to it.
 static hp_status decode_body(int b, int q, int h1, int h2, int heads, const hp_layer& w,
                              const void* t, int pos, const int32_t* dpos, const uint64_t* masks,
                              const hp_kv& kv, void* t_out, void* ws, const Ws& L, hipStream_t st,
-                             int topk_max_t = 0) {
+                             int topk_max_t = 0, const int32_t* rpos = nullptr) {
   const int64_t M = (int64_t)b * q;
   _Float16* qkv = at<_Float16>(ws, L.qkv);
   hp_status r;
   if ((r = launch_gemm(t, h1, w.wqkv, M, nullptr, 0, false, qkv, 3 * h1, at<void>(ws, L.part), st)) !=
       HP_OK)
     return r;
-  launch_kv_append(b, q, h1, heads, qkv, pos, dpos, kv, st);
+  launch_kv_append(b, q, h1, heads, qkv, pos, dpos, rpos, kv, st);
   if ((r = launch_ok("k_kv_append")) != HP_OK) return r;
   if (topk_max_t > 0) {
     if ((r = launch_topk_attention(b, h1, heads, qkv, pos, dpos, topk_max_t, 0, kv,
@@ -231,7 +341,7 @@ static hp_status decode_body(int b, int q, int h1, int h2, int heads, const hp_l
       return fail(r, "topk attention: bad row count");
     if ((r = launch_ok("k_topk_attn")) != HP_OK) return r;
   } else {
-    launch_decode_attention(b, q, h1, heads, qkv, pos, dpos, nullptr, masks, kv, at<void>(ws, L.a),
+    launch_decode_attention(b, q, h1, heads, qkv, pos, dpos, rpos, masks, kv, at<void>(ws, L.a),
                             st);
     if ((r = launch_ok("k_decode_attn")) != HP_OK) return r;
   }
@@ -241,6 +351,10 @@ static hp_status decode_body(int b, int q, int h1, int h2, int heads, const hp_l
 // Cache view of requests [r0, r0 + nb) of a layer's cache.
 static hp_kv kv_slice(const hp_kv& kv, int heads, int D, int64_t r0) {
   hp_kv o = kv;
+  if (kv.page_rows > 0) {  // the same pool; these requests' rows of the page table
+    o.pages = kv.pages + r0 * (kv.cap / kv.page_rows);
+    return o;
+  }
   const int64_t rows = r0 * heads * kv.cap;
   if (kv.fmt == HP_F16) {
     o.k = (char*)kv.k + rows * D * 2;
@@ -274,7 +388,7 @@ static hp_status decode_cells(int gbs, int nbat, const int* pos, const int* slot
   for (int c = 0; c < nbat; ++c) {
     const _Float16* qc = qkv + (int64_t)c * gbs * 3 * h1;
     const hp_kv kc = kv_slice(kv, heads, D, (int64_t)slot[c] * gbs);
-    launch_kv_append(gbs, 1, h1, heads, qc, pos[c], nullptr, kc, st);
+    launch_kv_append(gbs, 1, h1, heads, qc, pos[c], nullptr, nullptr, kc, st);
     if ((r = launch_ok("k_kv_append")) != HP_OK) return r;
     _Float16* ac = att + (int64_t)c * gbs * h1;
     if (topk_max_t > 0) {
@@ -450,10 +564,27 @@ hp_status hp_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const vo
   if (D != 64 && D != 128) return fail(HP_ERR_SHAPE, "head dim %d not in {64, 128}", D);
   if (!qkv) return fail(HP_ERR_NULL, "qkv is NULL");
   NEED_ALIGN(qkv, 16);
-  hp_status s = check_kv(kv, pos + q);
+  hp_status s = check_kv(kv, pos + q, 1);
   if (s != HP_OK) return s;
   if ((s = device_check()) != HP_OK) return s;
-  launch_kv_append(b, q, h1, heads, qkv, pos, nullptr, *kv, S(stream));
+  launch_kv_append(b, q, h1, heads, qkv, pos, nullptr, nullptr, *kv, S(stream));
+  return launch_ok("k_kv_append");
+}
+
+hp_status hp_kv_append_ragged(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
+                              const int32_t* rpos, int32_t max_pos, const hp_kv* kv,
+                              void* stream) {
+  if (b <= 0 || q <= 0 || h1 <= 0 || heads <= 0 || h1 % heads || max_pos < 0)
+    return fail(HP_ERR_SHAPE, "bad sizes");
+  const int D = h1 / heads;
+  if (D != 64 && D != 128) return fail(HP_ERR_SHAPE, "head dim %d not in {64, 128}", D);
+  if (!qkv || !rpos) return fail(HP_ERR_NULL, "NULL pointer");
+  NEED_ALIGN(qkv, 16);
+  NEED_ALIGN(rpos, 4);
+  hp_status s = check_kv(kv, max_pos + q, 1);
+  if (s != HP_OK) return s;
+  if ((s = device_check()) != HP_OK) return s;
+  launch_kv_append(b, q, h1, heads, qkv, max_pos, nullptr, rpos, *kv, S(stream));
   return launch_ok("k_kv_append");
 }
 
@@ -482,7 +613,7 @@ hp_status hp_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, c
   NEED_ALIGN(qkv, 16);
   NEED_ALIGN(out, 16);
   if (masks) NEED_ALIGN(masks, 8);
-  hp_status s = check_kv(kv, pos + q);
+  hp_status s = check_kv(kv, pos + q, kv && streaming_attention(kv, q) ? 1 : 0);
   if (s != HP_OK) return s;
   if ((s = device_check()) != HP_OK) return s;
   launch_decode_attention(b, q, h1, heads, qkv, pos, nullptr, nullptr, masks, *kv, out, S(stream));
@@ -503,7 +634,7 @@ hp_status hp_decode_attention_ragged(int32_t b, int32_t q, int32_t h1, int32_t h
   NEED_ALIGN(out, 16);
   NEED_ALIGN(prefix, 4);
   if (masks) NEED_ALIGN(masks, 8);
-  hp_status s = check_kv(kv, max_prefix + q);
+  hp_status s = check_kv(kv, max_prefix + q, kv && streaming_attention(kv, q) ? 1 : 0);
   if (s != HP_OK) return s;
   if ((s = device_check()) != HP_OK) return s;
   launch_decode_attention(b, q, h1, heads, qkv, max_prefix, nullptr, prefix, masks, *kv, out,
@@ -613,7 +744,7 @@ hp_status hp_layer_prefill(const hp_dims* d, const hp_layer* w, const void* x, c
   NEED_ALIGN(x_out, 16);
   NEED_ALIGN(ws, 256);
   if ((s = check_layer(*w, d->h1, d->h2)) != HP_OK) return s;
-  if ((s = check_kv(kv, d->s)) != HP_OK) return s;
+  if ((s = check_kv(kv, d->s, 1)) != HP_OK) return s;
   const Ws L = ws_layout(*d);
   if (ws_bytes < L.total) return fail(HP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   if ((s = device_check()) != HP_OK) return s;
@@ -636,7 +767,7 @@ hp_status hp_layer_decode(const hp_dims* d, const hp_layer* w, const void* t, in
   if (q < 1 || q > 64) return fail(HP_ERR_TREE, "q must be in [1, 64]");
   if (pos < 0) return fail(HP_ERR_SHAPE, "pos < 0");
   if ((s = check_layer(*w, d->h1, d->h2)) != HP_OK) return s;
-  if ((s = check_kv(kv, pos + q)) != HP_OK) return s;
+  if ((s = check_kv(kv, pos + q, kv && streaming_attention(kv, q) ? 1 : 0)) != HP_OK) return s;
   const Ws L = ws_layout(*d);
   if (ws_bytes < L.total) return fail(HP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   if ((s = device_check()) != HP_OK) return s;
@@ -682,10 +813,18 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   NEED_ALIGN(t_in, 16);
   NEED_ALIGN(t_out, 16);
   NEED_ALIGN(ws, 256);
+  // HP_DIAGONAL with page pools: every layer's pool has the same geometry
+  const bool paged = (flags & HP_DIAGONAL) && kv[0].page_rows > 0;
   for (int j = 0; j < d->l; ++j) {
     if ((s = check_layer(layers[j], d->h1, d->h2)) != HP_OK) return s;
-    if ((s = check_kv(&kv[j], d->s + d->n)) != HP_OK) return s;
+    if ((s = check_kv(&kv[j], d->s + d->n, paged ? 2 : 0)) != HP_OK) return s;
+    if (paged && (kv[j].page_rows != kv[0].page_rows || kv[j].cap != kv[0].cap ||
+                  kv[j].pool_pages != kv[0].pool_pages))
+      return fail(HP_ERR_SHAPE, "kv[%d]: page pools of different geometry", j);
   }
+  if (paged && kv[0].cap != (int)(cdiv(d->s + d->n, kv[0].page_rows) * kv[0].page_rows))
+    return fail(HP_ERR_SHAPE, "paged pools: cap must be s + n rounded up to page_rows");
+  if (paged && (flags & HP_TOPK10)) return fail(HP_ERR_SHAPE, "paged pools take no HP_TOPK10");
   const Ws L = ws_layout(*d);
   if (ws_bytes < L.total) return fail(HP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   const bool rbr = flags & HP_ROW_BY_ROW, mb = flags & HP_MICROBATCH;
@@ -778,6 +917,71 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
       }
     }
     return finish(launch_ok("row-by-row"));
+  }
+
+  if (diag && paged) {
+    // diagonal block schedule ([FlexGen] appendix A.2, Fig. 5) with every live
+    // request holding only the cache pages of its current length (the page's
+    // peak-memory formula).  The static schedule fixes every page on the host;
+    // the table goes to the workspace before the timed region.  Per iteration:
+    // the live requests' inputs and row positions are gathered (one kernel),
+    // then each layer runs the starting batch's prefill and one product,
+    // append and attention for all live decode requests (each at its own
+    // row), and the last layer's rows go to t_out (one kernel).
+    const int PR = kv[0].page_rows, ppr = kv[0].cap / PR;
+    std::vector<int32_t> table;
+    const int64_t need = diag_page_plan(*d, PR, kv[0].cap, &table);
+    if (need > kv[0].pool_pages)
+      return finish(fail(HP_ERR_CAPACITY, "page pools hold %d pages, the schedule needs %lld",
+                         kv[0].pool_pages, (long long)need));
+    int32_t* dpt = at<int32_t>(ws, L.pt);
+    int32_t* rpos = at<int32_t>(ws, L.rpos);
+    if ((size_t)d->b * ppr > (size_t)d->b * cdiv(d->s + d->n, 64))
+      return finish(fail(HP_ERR_SHAPE, "page table larger than its workspace region"));
+    if ((s = hip_ok(hipMemcpyAsync(dpt, table.data(), table.size() * 4, hipMemcpyHostToDevice, st),
+                    "hipMemcpyAsync")) != HP_OK ||
+        (s = hip_ok(hipStreamSynchronize(st), "hipStreamSynchronize")) != HP_OK)
+      return finish(s);
+    if (times_ms && (s = hip_ok(hipEventRecord(ev[1], st), "hipEventRecord")) != HP_OK)
+      return finish(s);
+    const _Float16* last = (d->l % 2 == 1) ? T1 : T0;
+    for (int it = 0; it < nbat + d->n; ++it) {
+      const int dlo = std::max(0, it - d->n), dhi = std::min(it - 1, nbat - 1);
+      const int M = (dhi - dlo + 1) * d->gbs;  // live decode requests
+      const int64_t r0 = (int64_t)dlo * d->gbs;
+      if (M > 0) {
+        launch_diag_rows(t_in, T0 + r0 * h1, rpos, M, (int)r0, d->gbs, d->b, d->s, it, d->h1, 0,
+                         st);
+        if ((s = launch_ok("k_diag_rows")) != HP_OK) return finish(s);
+      }
+      for (int j = 0; j < d->l; ++j) {
+        hp_kv kj = kv[j];
+        kj.pages = dpt;
+        if (it < nbat) {
+          const int64_t p0 = (int64_t)it * d->gbs;
+          const _Float16* in = (j == 0) ? (const _Float16*)x
+                                        : (((d->l - j) % 2 == 0) ? (const _Float16*)x_out : xb);
+          _Float16* out = ((d->l - 1 - j) % 2 == 0) ? (_Float16*)x_out : xb;
+          if ((s = prefill_body(d->gbs, d->s, d->h1, d->h2, d->heads, layers[j], in + p0 * sh,
+                                kv_slice(kj, d->heads, D, p0), out + p0 * sh, ws, L, st)) != HP_OK)
+            return finish(s);
+        }
+        if (M > 0) {
+          const _Float16* in = (j % 2 == 0) ? T0 : T1;
+          _Float16* out = (j % 2 == 0) ? T1 : T0;
+          if ((s = decode_body(M, 1, d->h1, d->h2, d->heads, layers[j], in + r0 * h1,
+                               d->s + d->n - 1, nullptr, nullptr, kv_slice(kj, d->heads, D, r0),
+                               out + r0 * h1, ws, L, st, 0, rpos)) != HP_OK)
+            return finish(s);
+        }
+      }
+      if (M > 0) {
+        launch_diag_rows(last + r0 * h1, t_out, nullptr, M, (int)r0, d->gbs, d->b, d->s, it, d->h1,
+                         1, st);
+        if ((s = launch_ok("k_diag_rows")) != HP_OK) return finish(s);
+      }
+    }
+    return finish(HP_OK);
   }
 
   if (diag) {
@@ -923,6 +1127,12 @@ int32_t hp_profile_read(char* buf, size_t len) {
     buf[n] = 0;
   }
   return (int32_t)agg.size();
+}
+
+int64_t hp_diagonal_pages(const hp_dims* d, int32_t page_rows) {
+  if (check_dims(d) != HP_OK || page_rows <= 0 || page_rows % 64) return 0;
+  const int cap = (int)(cdiv(d->s + d->n, page_rows) * page_rows);
+  return diag_page_plan(*d, page_rows, cap, nullptr);
 }
 
 void hp_release_graphs(void) {

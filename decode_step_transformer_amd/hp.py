@@ -37,7 +37,8 @@ class hp_layer(C.Structure):
 
 class hp_kv(C.Structure):
     _fields_ = [("fmt", C.c_int32), ("cap", C.c_int32), ("k", C.c_void_p), ("v", C.c_void_p),
-                ("k_sm", C.c_void_p), ("v_sm", C.c_void_p)]
+                ("k_sm", C.c_void_p), ("v_sm", C.c_void_p), ("pages", C.c_void_p),
+                ("page_rows", C.c_int32), ("pool_pages", C.c_int32)]
 
 
 class hp_capture(C.Structure):
@@ -59,7 +60,7 @@ EXPORTS = [
     "hp_tree_prune", "hp_kv_compact",
     "hp_workspace_bytes", "hp_layer_prefill", "hp_layer_decode", "hp_run_block",
     "hp_release_graphs", "hp_weight_bytes", "hp_kv_bytes", "hp_profile", "hp_profile_read",
-    "hp_debug_set_capture",
+    "hp_debug_set_capture", "hp_kv_append_ragged", "hp_diagonal_pages",
 ]
 
 _lib = None
@@ -83,6 +84,7 @@ def lib():
             "hp_gemm": [_p, _i64, C.POINTER(hp_mat), _i64, _p, _i64, _i32, _p, _i64, _p, _sz, _p],
             "hp_gemm_noalloc": [_p, _i64, C.POINTER(hp_mat), _i64, _p, _i64, _i32, _p, _i64, _p],
             "hp_kv_append": [_i32, _i32, _i32, _i32, _p, _i32, C.POINTER(hp_kv), _p],
+            "hp_kv_append_ragged": [_i32, _i32, _i32, _i32, _p, _p, _i32, C.POINTER(hp_kv), _p],
             "hp_prefill_attention": [_i32, _i32, _i32, _i32, _p, _p, _p],
             "hp_decode_attention": [_i32, _i32, _i32, _i32, _p, _i32, _p, C.POINTER(hp_kv), _p, _p],
             "hp_topk_attention": [_i32, _i32, _i32, _p, _i32, _i32, C.POINTER(hp_kv), _p, _p, _p],
@@ -111,6 +113,8 @@ def lib():
         L.hp_kv_bytes.argtypes = [C.POINTER(hp_dims), _i32]
         L.hp_kv_bytes.restype = C.c_uint64
         L.hp_release_graphs.restype = None
+        L.hp_diagonal_pages.argtypes = [C.POINTER(hp_dims), _i32]
+        L.hp_diagonal_pages.restype = C.c_int64
         L.hp_debug_set_capture.argtypes = [C.POINTER(hp_capture)]
         L.hp_debug_set_capture.restype = _i32
         L.hp_profile.argtypes = [_i32]
@@ -242,23 +246,31 @@ def hp_gemm_noalloc(x: torch.Tensor, w: Mat, res=None, relu=False, out=None, str
 
 
 class KVCache:
-    """One layer's cache tensors in the library layout (see hp_kv)."""
+    """One layer's cache tensors in the library layout (see hp_kv).
 
-    def __init__(self, fmt, b, heads, cap, d, device="cuda"):
+    Contiguous: [b][heads][cap][row].  Paged (page_rows > 0): a pool of
+    pool_pages pages [page][heads][page_rows][row]; `pages` (device int32
+    [b][cap / page_rows], or None when hp_run_block assigns pages under
+    HP_DIAGONAL) maps request rows to pages."""
+
+    def __init__(self, fmt, b, heads, cap, d, device="cuda", page_rows=0, pool_pages=0,
+                 pages=None):
         self.fmt, self.b, self.heads, self.cap, self.d = fmt, b, heads, cap, d
+        self.page_rows, self.pool_pages, self.pages = page_rows, pool_pages, pages
+        lead = (pool_pages, heads, page_rows) if page_rows else (b, heads, cap)
         if fmt == HP_F16:
-            self.k = torch.zeros((b, heads, cap, d), dtype=torch.float16, device=device)
-            self.v = torch.zeros((b, heads, cap, d), dtype=torch.float16, device=device)
+            self.k = torch.zeros(lead + (d,), dtype=torch.float16, device=device)
+            self.v = torch.zeros(lead + (d,), dtype=torch.float16, device=device)
             self.k_sm = self.v_sm = None
         else:
-            self.k = torch.zeros((b, heads, cap, d // 2), dtype=torch.uint8, device=device)
-            self.v = torch.zeros((b, heads, cap, d // 2), dtype=torch.uint8, device=device)
-            self.k_sm = torch.zeros((b, heads, cap, d // 64, 2), dtype=torch.int16, device=device)
-            self.v_sm = torch.zeros((b, heads, cap, d // 64, 2), dtype=torch.int16, device=device)
+            self.k = torch.zeros(lead + (d // 2,), dtype=torch.uint8, device=device)
+            self.v = torch.zeros(lead + (d // 2,), dtype=torch.uint8, device=device)
+            self.k_sm = torch.zeros(lead + (d // 64, 2), dtype=torch.int16, device=device)
+            self.v_sm = torch.zeros(lead + (d // 64, 2), dtype=torch.int16, device=device)
 
     def c(self) -> hp_kv:
         return hp_kv(self.fmt, self.cap, _ptr(self.k), _ptr(self.v), _ptr(self.k_sm),
-                     _ptr(self.v_sm))
+                     _ptr(self.v_sm), _ptr(self.pages), self.page_rows, self.pool_pages)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.k, self.v, self.k_sm, self.v_sm)
@@ -268,6 +280,16 @@ class KVCache:
 def hp_kv_append(b, q, h1, heads, qkv, pos, kv: KVCache, stream=None):
     c = kv.c()
     _check(lib().hp_kv_append(b, q, h1, heads, _ptr(qkv), pos, C.byref(c), _stream(stream)))
+
+
+def hp_kv_append_ragged(b, q, h1, heads, qkv, rpos, max_pos, kv: KVCache, stream=None):
+    c = kv.c()
+    _check(lib().hp_kv_append_ragged(b, q, h1, heads, _ptr(qkv), _ptr(rpos), max_pos, C.byref(c),
+                                     _stream(stream)))
+
+
+def hp_diagonal_pages(d: hp_dims, page_rows: int) -> int:
+    return int(lib().hp_diagonal_pages(C.byref(d), page_rows))
 
 
 def hp_prefill_attention(b, s, h1, heads, qkv, out=None, stream=None):

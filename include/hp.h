@@ -112,10 +112,25 @@ typedef struct {
  *   HP_Q4:  k, v = u8 codes [b][heads][cap][d/2] (generic row layout, one
  *           row = one token of one head, groups of 64 channels),
  *           k_sm, v_sm = half2 {scale, min} [b][heads][cap][d/64].
- * All pointers are device memory; b is the request count of the call. */
+ * All pointers are device memory; b is the request count of the call.
+ *
+ * Paged caches (page_rows > 0): k, v, k_sm, v_sm are pools of pool_pages
+ * pages, page p holding page_rows rows of every head, [p][heads][page_rows]
+ * [row] in the layouts above; row j of request r, head h is row
+ * j % page_rows of page pages[r * (cap / page_rows) + j / page_rows]
+ * (device int32 [b][cap / page_rows]; entries outside [0, pool_pages) are
+ * clamped into it).  cap is then the logical rows per request, a multiple
+ * of page_rows; page_rows is a multiple of 64.  hp_kv_append and
+ * hp_decode_attention / hp_decode_attention_ragged with q < 16 take paged
+ * caches; the other cache calls return HP_ERR_SHAPE for them.  Under
+ * HP_DIAGONAL, hp_run_block assigns the pages itself (pages = NULL; see
+ * HP_DIAGONAL).  Contiguous caches: pages = NULL, page_rows = pool_pages
+ * = 0. */
 typedef struct {
   int32_t fmt, cap;
   void *k, *v, *k_sm, *v_sm;
+  const int32_t* pages;
+  int32_t page_rows, pool_pages;
 } hp_kv;
 
 typedef struct {
@@ -189,6 +204,14 @@ hp_status hp_gemm_noalloc(const void* x, int64_t ldx, const hp_mat* w, int64_t M
  * [2 h1, 3 h1).  Requires pos + q <= kv->cap. */
 hp_status hp_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
                        int32_t pos, const hp_kv* kv, void* stream);
+
+/* hp_kv_append with a row position per request (requests at different
+ * lengths, as in the diagonal block schedule): request r's token i goes to
+ * row rpos[r] + i, rpos: device int32 [b], each clamped to [0, max_pos].
+ * Requires max_pos + q <= kv->cap. */
+hp_status hp_kv_append_ragged(int32_t b, int32_t q, int32_t h1, int32_t heads, const void* qkv,
+                              const int32_t* rpos, int32_t max_pos, const hp_kv* kv,
+                              void* stream);
 
 /* Causal prefill attention over the fresh K/V ([FlexGen] prefill equations;
  * causal mask: query i sees keys 0..i).  qkv: device half [b][s][3 h1]
@@ -336,12 +359,23 @@ enum {
                         iteration; results equal the zig-zag block's bit for
                         bit when each product of the two schedules falls on
                         the same side of M = 144 rows (always for b <= 144),
-                        within rounding otherwise.  Batch k
-                        keeps its cache in slot k mod min(b / gbs, n + 1), so
-                        kv[j] needs only that many GPU batches of requests.
-                        Eager launches: not with HP_GRAPH, HP_ROW_BY_ROW or
-                        HP_MICROBATCH (HP_ERR_SHAPE).  times_ms[0] = 0,
-                        times_ms[1] = the whole schedule */
+                        within rounding otherwise.  Eager launches: not with
+                        HP_GRAPH, HP_ROW_BY_ROW or HP_MICROBATCH
+                        (HP_ERR_SHAPE).  times_ms[0] = 0, times_ms[1] = the
+                        whole schedule.  Two cache modes, set by kv[j]:
+                        - contiguous (page_rows 0): batch k keeps its cache
+                          in slot k mod min(b / gbs, n + 1), so kv[j] needs
+                          only that many GPU batches of requests (cap >=
+                          s + n); append and attention run per batch;
+                        - paged (page_rows > 0, pages NULL): kv[j] is a pool
+                          of pool_pages pages and every live request holds
+                          only the pages its current length needs (freed
+                          after its last step), so the pool follows the
+                          page's peak-memory formula instead of b (s + n)
+                          rows; hp_diagonal_pages() gives the pages needed.
+                          One product, append and attention per layer and
+                          iteration for all live batches.  Not with
+                          HP_TOPK10. */
 };
 
 /* [FlexGen] section 4, Algorithm 1: zig-zag block schedule over one block of
@@ -359,6 +393,13 @@ enum {
 hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, const void* t_in,
                        const hp_kv* kv, void* x_out, void* t_out, void* ws, size_t ws_bytes,
                        uint32_t flags, float* times_ms, void* stream);
+
+/* [FlexGen] appendix A.2 (diagonal block schedule, peak memory): the number of
+ * cache pages of page_rows rows (per request, all heads; a multiple of 64)
+ * that HP_DIAGONAL with paged caches holds at its peak for these dims: live
+ * requests hold ceil(current length / page_rows) pages each.  0 for invalid
+ * dims or page_rows. */
+int64_t hp_diagonal_pages(const hp_dims* d, int32_t page_rows);
 
 /* Drops every captured graph (device memory of graph execs is released). */
 void hp_release_graphs(void);

@@ -94,3 +94,34 @@ def test_gemm_noalloc_host_checks():
     assert hp.hp_gemm_workspace_bytes(144, 49152, 24576, hp.HP_Q4) > 64 << 20
     assert L.hp_gemm_noalloc(fake, 49152, C.byref(big), 144, None, 0, 0, fake, 24576, None) == -5
     assert "static scratch" in hp.hp_last_error()
+
+
+def _diag_pages_closed_form(b, s, n, gbs, pr):
+    """Pages in use at the busiest iteration of the diagonal schedule, counted directly:
+    at iteration it, GPU batch it (if any) holds its prompt rows and every batch k in
+    [it - n, it - 1] holds s + (it - k) rows, each request ceil(rows / pr) pages."""
+    nb = b // gbs
+    best = 0
+    for it in range(nb + n):
+        live = [s] if it < nb else []
+        live += [s + it - k for k in range(max(0, it - n), min(it - 1, nb - 1) + 1)]
+        best = max(best, gbs * sum(-(-rows // pr) for rows in live))
+    return best
+
+
+def test_diagonal_pages():
+    """[FlexGen] appendix A.2: the diagonal schedule's peak cache, in pages, from the
+    library's page plan equals a direct count over the iterations; with n >> s it
+    approaches half of what the same live requests hold at full length s + n (the
+    page's (2s + n) / 2 against s + n)."""
+    from decode_step_transformer_amd import hp
+    for b, s, n, gbs, pr in ((12, 20, 7, 3, 64), (150, 16, 128, 1, 64), (144, 512, 32, 48, 64),
+                             (40, 100, 300, 2, 128), (512, 32, 480, 1, 64)):
+        d = hp.dims(b, s, n, 256, 512, 2, 4, gbs)
+        assert hp.hp_diagonal_pages(d, pr) == _diag_pages_closed_form(b, s, n, gbs, pr), (b, s, n)
+    d = hp.dims(512, 32, 480, 256, 512, 2, 4, 1)
+    live = 481                                         # n + 1 requests in steady state
+    full = live * (32 + 480)                           # their rows at full length
+    paged = hp.hp_diagonal_pages(d, 64) * 64
+    assert 0.5 < paged / full < 0.6
+    assert hp.hp_diagonal_pages(d, 48) == 0            # page rows must be a multiple of 64
