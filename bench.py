@@ -233,12 +233,13 @@ def prefill_products_finite(hp, torch, stream, c, layers):
     return res
 
 
-def quant_kernels(hp, torch, stream, c, reps=10):
+def quant_kernels(hp, torch, stream, c, cname, reps=10):
     """The int4 group-64 coder ([FlexGen] section 5) at its two uses: hp_quantize_g64
     on a weight of the 175B shape (w1, 12288 x 49152) and of this configuration, and
     hp_kv_append at the prefill shape (b*s tokens) and the decode shape (b tokens),
     event-timed over `reps` launches on finite seeded data.  HBM bytes per element:
     2 read + 0.5625 written (codes + fp16 scale/min per group of 64)."""
+    from decode_step_transformer_amd import traffic as tr
     b, s, h1, H = c["b"], c["s"], c["h1"], c["heads"]
     g = torch.Generator(device="cuda")
     g.manual_seed(23)
@@ -264,6 +265,7 @@ def quant_kernels(hp, torch, stream, c, reps=10):
         by = k * n * 2.5625
         out[name] = {"shape": [k, n], "avg_us": ms * 1e3, "gbs": by / (ms / 1e3) / 1e9,
                      "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+    out["quantize_175b_w1"]["traffic"] = tr.lookup("k_quantize_g64", "quant-175b-w1")
         del w, codes, sm
     if c["fmt"] == 1:
         kv = hp.KVCache(1, b, H, s + 1, h1 // H)
@@ -272,7 +274,8 @@ def quant_kernels(hp, torch, stream, c, reps=10):
         by = 2 * b * s * h1 * 2.5625
         out["kv_append_prefill"] = {"tokens": b * s, "avg_us": ms * 1e3,
                                     "gbs": by / (ms / 1e3) / 1e9,
-                                    "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+                                    "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                    "traffic": tr.lookup("k_kv_append", cname)}
         q1 = qkv[:, :1].contiguous()
         ms = ev_ms(lambda: hp.hp_kv_append(b, 1, h1, H, q1, s, kv, stream=stream), 5 * reps)
         out["kv_append_decode"] = {"tokens": b, "avg_us": ms * 1e3,
@@ -457,11 +460,13 @@ def tree_attention(hp, torch, stream, reps=20):
     cache_bytes = 2.0 * b * H * (P + q) * (D / 2 + 4 * D / 64)
     flops = 4.0 * D * b * H * q * P                       # prefix part; tree rows add < 2%
     prune = tree_prune_step(hp, torch, stream, g, parent.cuda(), kv, reps)
+    from decode_step_transformer_amd import traffic as tr
     return {"workload": f"tree-masked decode attention b={b} h1={h1} heads={H} prefix={P} q={q} "
                         "int4 cache",
             "avg_us": ms * 1e3, "bound": "hbm", "gbs": cache_bytes / (ms / 1e3) / 1e9,
             "frac_hbm": cache_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             "tflops": flops / (ms / 1e3) / 1e12,
+            "traffic": tr.lookup("k_multi_attn", "tree"),
             "work": "cache bytes 2*b*heads*(prefix+q)*(d/2 + 4*d/64) per launch, one read",
             "prune": prune}
 
@@ -627,7 +632,7 @@ def main():
         log("sparse attention (finite caches)")
         sparse = sparse_attention(hp, torch, stream, c, kvs, args.config)
         log("quantiser and KV append")
-        qk = quant_kernels(hp, torch, stream, c)
+        qk = quant_kernels(hp, torch, stream, c, args.config)
         log("prefill products (finite)")
         pgemm = prefill_products_finite(hp, torch, stream, c, layers)
         topk_block = None

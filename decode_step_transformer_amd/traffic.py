@@ -25,7 +25,10 @@ launch), so its GEMM launches have the block's shapes.  `decode` runs one
 layer decode the same way, at the cache length where bench.py times the
 decode kernels (the decode GEMM and attention; select them with
 --kernel-include-regex 'k_gemm_dq|k_decode_attn').  `topk` runs Top-K sparse
-attention at the same cache length (k_topk_attn).
+attention at the same cache length (k_topk_attn).  `tree` runs the
+tree-masked decode attention workload (k_multi_attn) and `quant` the int4
+quantiser on a weight of the 175B w1 shape (k_quantize_g64); `prefill` also
+covers the KV append at the prefill shape (k_kv_append).
 
 `summarize` writes profiles/traffic.json: per kernel, the calibrated bytes
 read and written per dispatch and a hash of the sources that define the
@@ -51,6 +54,9 @@ KERNEL_SOURCES = {
     "k_gemm_dq": ["csrc/gemm_dec.hip", "csrc/lds_dma.h", "csrc/dequant_dev.h", "csrc/common.h"],
     "k_decode_attn": ["csrc/attn.hip", "csrc/decode_dev.h", "csrc/dequant_dev.h", "csrc/common.h"],
     "k_topk_attn": ["csrc/topk.hip", "csrc/decode_dev.h", "csrc/dequant_dev.h", "csrc/common.h"],
+    "k_multi_attn": ["csrc/attn.hip", "csrc/lds_dma.h", "csrc/dequant_dev.h", "csrc/common.h"],
+    "k_kv_append": ["csrc/attn.hip", "csrc/quant_dev.h", "csrc/common.h"],
+    "k_quantize_g64": ["csrc/quant.hip", "csrc/quant_dev.h", "csrc/common.h"],
 }
 
 
@@ -144,6 +150,54 @@ def topk(config: str, calls: int = 2) -> None:
         print(f"topk call {i} done", flush=True)
 
 
+def tree(calls: int = 3) -> None:
+    """The tree-masked decode attention workload of bench.py (8 requests, h1 = 8192,
+    64 heads, 2048-row int4 prefix, 64 tree tokens with random BFS parents):
+    `calls` hp_decode_attention calls (k_multi_attn)."""
+    import torch
+
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    from bench import TREE
+    from decode_step_transformer_amd import hp
+
+    b, h1, H, P, q = TREE["b"], TREE["h1"], TREE["heads"], TREE["prefix"], TREE["q"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    sig = 0.02 * h1 ** 0.5
+    kv = hp.KVCache(1, b, H, P + q, h1 // H)
+    pre = (torch.randn((b, P, 3 * h1), generator=g, device="cuda") * sig).half()
+    hp.hp_kv_append(b, P, h1, H, pre, 0, kv)
+    del pre
+    qkv = (torch.randn((b, q, 3 * h1), generator=g, device="cuda") * sig).half()
+    hp.hp_kv_append(b, q, h1, H, qkv, P, kv)
+    parent = torch.arange(-1, q - 1, dtype=torch.int32).repeat(b, 1)
+    parent[:, 1:] = torch.div(torch.arange(0, q - 1), 2, rounding_mode="floor").to(torch.int32)
+    masks, _ = hp.hp_tree_masks(parent.cuda())
+    for i in range(calls):
+        hp.hp_decode_attention(b, q, h1, H, qkv, P, kv, masks=masks)
+        torch.cuda.synchronize()
+        print(f"tree call {i} done", flush=True)
+
+
+def quant(calls: int = 3) -> None:
+    """hp_quantize_g64 on an fp16 weight of the 175B w1 shape (12288 x 49152)."""
+    import torch
+
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    from decode_step_transformer_amd import hp
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(23)
+    w = (torch.randn((12288, 49152), generator=g, device="cuda") * 0.02).half()
+    torch.cuda.synchronize()
+    for i in range(calls):
+        hp.hp_quantize_g64(w)
+        torch.cuda.synchronize()
+        print(f"quantize call {i} done", flush=True)
+
+
 def _config_n(config: str) -> int:
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
@@ -209,6 +263,10 @@ if __name__ == "__main__":
         decode(sys.argv[2])
     elif len(sys.argv) == 3 and sys.argv[1] == "topk":
         topk(sys.argv[2])
+    elif len(sys.argv) == 2 and sys.argv[1] == "tree":
+        tree()
+    elif len(sys.argv) == 2 and sys.argv[1] == "quant":
+        quant()
     elif len(sys.argv) == 8 and sys.argv[1] == "summarize":
         print(json.dumps(summarize(*sys.argv[2:8]), indent=1))
     else:
