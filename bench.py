@@ -265,8 +265,8 @@ def quant_kernels(hp, torch, stream, c, cname, reps=10):
         by = k * n * 2.5625
         out[name] = {"shape": [k, n], "avg_us": ms * 1e3, "gbs": by / (ms / 1e3) / 1e9,
                      "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
-    out["quantize_175b_w1"]["traffic"] = tr.lookup("k_quantize_g64", "quant-175b-w1")
         del w, codes, sm
+    out["quantize_175b_w1"]["traffic"] = tr.lookup("k_quantize_g64", "quant-175b-w1")
     if c["fmt"] == 1:
         kv = hp.KVCache(1, b, H, s + 1, h1 // H)
         qkv = (torch.randn((b, s, 3 * h1), generator=g, device="cuda") * 0.02 * h1 ** 0.5).half()
