@@ -22,11 +22,16 @@
 namespace hp {
 
 // ------------------------------------------------------------ KV append
-// One block row of the grid per new token (request r, token i): the token's K
-// and V columns are 2 h1 contiguous halves of its qkv row, i.e. 2 h1 / 64
-// groups; blockIdx.y picks a run of 32 AU groups of them, a lane codes AU
-// groups (loads issued first) and writes each into the head-major cache row
-// of its head.
+// A workgroup codes 32 AU groups of 64 channels of one new token's K | V
+// columns (2 h1 contiguous halves: a wave reads 1 KB contiguous; a lane codes
+// AU groups, their loads issued first) and writes each group into the
+// head-major cache row of its head.  Neighbouring rows of one head share
+// cache lines, so the workgroups of TQ consecutive tokens (TQ = 16: 1 KB of
+// codes and 128 B of scale/min pairs per head) are given ids of one residue
+// mod 8: workgroup ids reach the 8 XCDs round-robin, so those rows are all
+// written through one XCD's L2, which gathers the pieces of each line before
+// writing it back (with consecutive ids, neighbouring rows came through
+// different L2s and reached HBM as partial lines).
 struct AppendArgs {
   const _Float16* qkv;
   int b, q, h1, H, D, pos;
@@ -56,12 +61,19 @@ template <bool Q4, int D>
 __global__ __launch_bounds__(256) void k_kv_append(AppendArgs a) {
   constexpr int G = D / 64;  // groups per head row
   const int sub = threadIdx.x & 7;
-  const int token = blockIdx.x;  // r * q + i
+  const int HG = a.H * G;    // groups of K (and of V) per token
+  const int SC = (2 * HG + 32 * AU - 1) / (32 * AU);  // workgroups per token
+  // id -> (chunk of 16 tokens, token, span piece): the 16 SC workgroups of a
+  // chunk are the ids x, x + 8, x + 16, ... of one residue x
+  const int id = blockIdx.x, x = id & 7, k = id >> 3;
+  const int per = 16 * SC;
+  const int chunk = x + 8 * (k / per), within = k % per;
+  const int token = chunk * 16 + within / SC, sc = within % SC;  // token = r * q + i
+  if (token >= a.b * a.q) return;
   const int r = token / a.q, i = token % a.q;
-  const int HG = a.H * G;        // groups of K (and of V) per token
   const int pos = a.rpos ? min(max(a.rpos[r], 0), a.pos) : a.pos + (a.dpos ? *a.dpos : 0);
   const _Float16* src = a.qkv + (int64_t)token * 3 * a.h1 + a.h1;  // K | V of this token
-  const int gg0 = blockIdx.y * (32 * AU) + (threadIdx.x >> 3);
+  const int gg0 = sc * (32 * AU) + (threadIdx.x >> 3);
   uint4 raw[AU];
 #pragma unroll
   for (int u = 0; u < AU; ++u) {
@@ -579,7 +591,9 @@ void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const voi
                kv.page_rows > 0 ? kv.pages : nullptr, kv.page_rows, kv.pool_pages};
   const int64_t tokens = (int64_t)b * q;
   if (tokens == 0) return;
-  const dim3 grid((unsigned)tokens, (unsigned)cdiv(2 * (h1 / 64), 32 * AU));
+  const int64_t sc = cdiv(2 * (h1 / 64), 32 * AU);     // workgroups per token
+  const int64_t chunks = cdiv(tokens, 16);               // chunks of 16 tokens
+  const dim3 grid((unsigned)(8 * cdiv(chunks, 8) * 16 * sc));
   Prof prof(kv.fmt == HP_Q4 ? "kv_append_q4" : "kv_append_f16", st);
   const int D = h1 / heads;
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a); };
