@@ -323,11 +323,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dq(DqArgs g) {
 // epilogue.  Partial layout: [split][column tile][column group][row tile]
 // [subtile][lane] f32x4, lane l holding row 16 (row tile) + l % 16 and
 // columns 16 (subtile) + 4 (l / 16) .. +3 of its group; one thread per f32x4
-// of a split, so the partial reads are contiguous.
-__global__ __launch_bounds__(256) void k_dq_reduce(const float* __restrict__ P, int splits,
-                                                   int ntiles, int tm, int M, int N,
-                                                   const _Float16* __restrict__ res, int64_t ldr,
-                                                   int relu, _Float16* __restrict__ Y,
+// of a split, so the partial reads are contiguous.  The split count is a
+// template argument: a thread issues the loads of all S splits before the
+// first add (a run-time loop waits for each load in turn), and the adds
+// still go in split order.
+template <int S>
+__global__ __launch_bounds__(256) void k_dq_reduce(const float* __restrict__ P, int ntiles, int tm,
+                                                   int M, int N, const _Float16* __restrict__ res,
+                                                   int64_t ldr, int relu, _Float16* __restrict__ Y,
                                                    int64_t ldy) {
   const int64_t per_split = (int64_t)ntiles * 4 * tm * 4 * 64;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -340,8 +343,12 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const float* __restrict__ P, 
     const int m = 16 * i + (lane & 15);
     const int n = nt * 256 + wcol * 64 + 16 * t + 4 * (lane >> 4);
     if (m >= M || n >= N) continue;
-    f32x4 v = *(const f32x4*)(P + q * 4);
-    for (int s = 1; s < splits; ++s) v += *(const f32x4*)(P + (s * per_split + q) * 4);
+    f32x4 p[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) p[s] = __builtin_nontemporal_load((const f32x4*)(P + (s * per_split + q) * 4));
+    f32x4 v = p[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) v += p[s];
     if (relu) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
@@ -355,6 +362,21 @@ __global__ __launch_bounds__(256) void k_dq_reduce(const float* __restrict__ P, 
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = (_Float16)v[e];
     *(f16x4*)(Y + m * ldy + n) = o;
+  }
+}
+
+template <int N = 2, class F>
+bool with_splits(int n, F&& f) {
+  if constexpr (N > 16) {
+    (void)n;
+    (void)f;
+    return false;
+  } else {
+    if (n == N) {
+      f(std::integral_constant<int, N>());
+      return true;
+    }
+    return with_splits<N + 1>(n, f);
   }
 }
 
@@ -402,9 +424,12 @@ hp_status launch_gemm_dq(const void* x, int64_t ldx, const hp_mat& w, int64_t M,
   const int64_t per_split = (int64_t)a.ntiles * 4 * T * 4 * 64;
   const int blocks = (int)std::min<int64_t>(cdiv(per_split, 256), 8192);
   Prof prof_r("gemm_splitk_reduce", st);
-  hipLaunchKernelGGL(k_dq_reduce, dim3(blocks), dim3(256), 0, st, (const float*)partials, splits,
-                     a.ntiles, T, (int)M, w.n, (const _Float16*)res, ldr, a.relu, (_Float16*)y,
-                     ldy);
+  const bool known = with_splits(splits, [&](auto s_) {
+    hipLaunchKernelGGL(k_dq_reduce<decltype(s_)::value>, dim3(blocks), dim3(256), 0, st,
+                       (const float*)partials, a.ntiles, T, (int)M, w.n, (const _Float16*)res, ldr,
+                       a.relu, (_Float16*)y, ldy);
+  });
+  if (!known) return fail(HP_ERR_SHAPE, "split count %d outside 2..16", splits);
   return launch_ok("k_dq_reduce");
 }
 

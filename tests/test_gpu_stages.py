@@ -229,6 +229,18 @@ def _decode(hp, orc, cid, j):
     finally:
         hp.hp_debug_set_capture(off=True)
     torch.cuda.synchronize()
+    # every request of the batch: the layer's four products against the
+    # standalone product on the same fp16 inputs, bit for bit (a row's result
+    # depends neither on the caller nor on the workspace it runs in)
+    t0, o0 = t[:, 0], to[:, 0]
+    for xin, mat, res, relu, got, name in (
+            (t0, layer.wqkv, None, False, cap["qkv"], "QKV"),
+            (cap["attn"], layer.wo, t0, False, cap["x_out"], "x_out"),
+            (cap["x_out"], layer.w1, None, True, cap["hidden"], "hidden"),
+            (cap["hidden"], layer.w2, cap["x_out"], False, o0, "output")):
+        ref = hp.hp_gemm(xin, mat, res=res, relu=relu)
+        assert torch.equal(ref.view(torch.int16), got.view(torch.int16)), \
+            f"config {cid} layer {j} decode {name}: the layer's product differs from hp_gemm"
     ridx = list(req)
     Q, A = host(cap["qkv"])[ridx], host(cap["attn"])[ridx]
     XO, HID, Y = host(cap["x_out"])[ridx], host(cap["hidden"])[ridx], host(to)[ridx, 0]
