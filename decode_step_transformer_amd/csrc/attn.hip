@@ -101,6 +101,74 @@ __global__ __launch_bounds__(256) void k_kv_append(AppendArgs a) {
   }
 }
 
+// Tiled int4 append for whole chunks of rows (prefill and multi-token
+// appends into a contiguous cache, d = 128, rows starting at a multiple of
+// 16): one workgroup per (request, 16 consecutive tokens, 4 heads).  The
+// 8 lanes of a group code it as k_kv_append does (the same coder, the same
+// bits).  Group (slot u, wave w, octet j): tile (head, K or V) = (4 u + w) / 4,
+// rows 4 ((4 u + w) % 4) + j / 2 of the chunk, group j % 2 of the row, so one
+// store instruction writes 4 consecutive cache rows of one head: 256
+// contiguous bytes of codes.  The scale/min words of a tile (16 rows x 2
+// groups, 128 contiguous bytes in the cache) meet in LDS in cache order and
+// leave as 16-byte stores: every memory write covers whole 64-byte pieces, so
+// none needs the memory's read-modify-write of a partial piece.
+constexpr int KT_ROWS = 16, KT_HEADS = 4;
+constexpr int KT_SLOTS = 2 * KT_HEADS;  // (heads x (K, V) x 4 row quads) / 4 waves groups per lane
+
+__global__ __launch_bounds__(256) void k_kv_append_tile(AppendArgs a) {
+  __shared__ uint32_t sml[4 * KT_SLOTS][8];  // [tile * 4 + row quad][octet]: cache order per tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane >> 3, sub = lane & 7;
+  const int nhb = (a.H + KT_HEADS - 1) / KT_HEADS, nch = (a.q + KT_ROWS - 1) / KT_ROWS;
+  const int hb = blockIdx.x % nhb, rc = blockIdx.x / nhb;
+  const int c = rc % nch, r = rc / nch;
+  const int i0 = c * KT_ROWS;
+  uint4 raw[KT_SLOTS];
+#pragma unroll
+  for (int u = 0; u < KT_SLOTS; ++u) {
+    const int idx = 4 * u + w;
+    const int h = hb * KT_HEADS + (idx >> 3), which = (idx >> 2) & 1;
+    const int i = i0 + 4 * (idx & 3) + (j >> 1);
+    const int ii = min(i, a.q - 1), hh = min(h, a.H - 1);  // rows and heads past the end re-read
+    const _Float16* src = a.qkv + ((int64_t)r * a.q + ii) * 3 * a.h1 + (int64_t)a.h1 * (1 + which) +
+                          hh * 128 + 64 * (j & 1);
+    raw[u] = stream_load16((const uint4*)src + sub);
+  }
+#pragma unroll
+  for (int u = 0; u < KT_SLOTS; ++u) {
+    const int idx = 4 * u + w;
+    const int h = hb * KT_HEADS + (idx >> 3), which = (idx >> 2) & 1;
+    const int i = i0 + 4 * (idx & 3) + (j >> 1);
+    uint32_t smw;
+    const uint32_t word = quant_group8(raw[u], smw);
+    if (sub == 0) sml[idx][j] = smw;
+    if (i < a.q && h < a.H) {
+      const int64_t row = ((int64_t)r * a.H + h) * a.cap + a.pos + i;
+      uint8_t* dst = (uint8_t*)(which ? a.v : a.k) + row * 64 + 32 * (j & 1);
+      __builtin_nontemporal_store(word, (uint32_t*)(dst + 4 * sub));  // streamed out
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 16 * KT_HEADS) {
+    // 2 KT_HEADS tiles x 128 bytes: thread -> tile t / 8, bytes 16 (t % 8) ..
+    // +15 (rows 2 (t % 8) and 2 (t % 8) + 1 of the chunk)
+    const int tile = threadIdx.x >> 3, part = threadIdx.x & 7;
+    const int h = hb * KT_HEADS + (tile >> 1), which = tile & 1;
+    const int i = i0 + 2 * part;
+    if (h < a.H && i < a.q) {
+      const uint32_t* s4 = &sml[4 * tile + (part >> 1)][4 * (part & 1)];
+      const int64_t row = ((int64_t)r * a.H + h) * a.cap + a.pos + i;
+      uint32_t* dst = (which ? a.vsm : a.ksm) + row * 2;
+      if (i + 1 < a.q) {
+        *(uint4*)dst = make_uint4(s4[0], s4[1], s4[2], s4[3]);
+      } else {
+        dst[0] = s4[0];
+        dst[1] = s4[1];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------- decode attention
 struct DecArgs {
   const _Float16* qkv;
@@ -591,11 +659,18 @@ void launch_kv_append(int32_t b, int32_t q, int32_t h1, int32_t heads, const voi
                kv.page_rows > 0 ? kv.pages : nullptr, kv.page_rows, kv.pool_pages};
   const int64_t tokens = (int64_t)b * q;
   if (tokens == 0) return;
+  const int D = h1 / heads;
+  if (kv.fmt == HP_Q4 && D == 128 && q >= KT_ROWS && !dpos && !rpos && kv.page_rows == 0 &&
+      pos % KT_ROWS == 0 && kv.cap % KT_ROWS == 0) {
+    const int64_t grid = (int64_t)b * cdiv(q, KT_ROWS) * cdiv(heads, KT_HEADS);
+    Prof prof("kv_append_q4", st);
+    hipLaunchKernelGGL(k_kv_append_tile, dim3((unsigned)grid), dim3(256), 0, st, a);
+    return;
+  }
   const int64_t sc = cdiv(2 * (h1 / 64), 32 * AU);     // workgroups per token
   const int64_t chunks = cdiv(tokens, 16);               // chunks of 16 tokens
   const dim3 grid((unsigned)(8 * cdiv(chunks, 8) * 16 * sc));
   Prof prof(kv.fmt == HP_Q4 ? "kv_append_q4" : "kv_append_f16", st);
-  const int D = h1 / heads;
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a); };
   if (kv.fmt == HP_Q4)
     D == 128 ? go(k_kv_append<true, 128>) : go(k_kv_append<true, 64>);

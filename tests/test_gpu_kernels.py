@@ -141,8 +141,12 @@ def _qkv(seed, b, q, h1):
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
-@pytest.mark.parametrize("b,q,h1,heads,pos,cap", [(2, 5, 256, 4, 0, 8), (3, 1, 256, 2, 7, 9),
-                                                  (1, 64, 512, 4, 100, 170)])
+@pytest.mark.parametrize("b,q,h1,heads,pos,cap", [
+    (2, 5, 256, 4, 0, 8), (3, 1, 256, 2, 7, 9), (1, 64, 512, 4, 100, 170),
+    # d = 128, rows from a multiple of 16 (the tiled int4 append: 16 tokens x 4 heads
+    # per workgroup): whole chunks and head blocks; a ragged last chunk with a partial
+    # head block; fewer heads than a block
+    (2, 48, 1024, 8, 0, 64), (3, 37, 768, 6, 16, 64), (1, 16, 256, 2, 32, 48)])
 def test_kv_append_bit_exact(hp, orc, fmt, b, q, h1, heads, pos, cap):
     qkv = _qkv(60 + q, b, q, h1)
     D = h1 // heads
