@@ -268,7 +268,7 @@ def quant_kernels(hp, torch, stream, c, cname, reps=10):
         del w, codes, sm
     out["quantize_175b_w1"]["traffic"] = tr.lookup("k_quantize_g64", "quant-175b-w1")
     if c["fmt"] == 1:
-        kv = hp.KVCache(1, b, H, s + 1, h1 // H)
+        kv = hp.KVCache(1, b, H, s + c["n"], h1 // H)  # the block's cache geometry
         qkv = (torch.randn((b, s, 3 * h1), generator=g, device="cuda") * 0.02 * h1 ** 0.5).half()
         ms = ev_ms(lambda: hp.hp_kv_append(b, s, h1, H, qkv, 0, kv, stream=stream), reps)
         by = 2 * b * s * h1 * 2.5625
@@ -282,6 +282,18 @@ def quant_kernels(hp, torch, stream, c, cname, reps=10):
                                    "note": "launch-bound (%.1f MB per launch)"
                                            % (2 * b * h1 * 2.5625 / 1e6)}
         del kv, qkv, q1
+        # the same append at the OPT-175B prefill shape (h1 = 12288, 96 heads)
+        c2 = CONFIGS["opt-175b-int4"]
+        h2_, H2 = c2["h1"], c2["heads"]
+        kv = hp.KVCache(1, b, H2, s + c2["n"], h2_ // H2)
+        qkv = (torch.randn((b, s, 3 * h2_), generator=g, device="cuda") * 0.02 * h2_ ** 0.5).half()
+        ms = ev_ms(lambda: hp.hp_kv_append(b, s, h2_, H2, qkv, 0, kv, stream=stream), reps)
+        by = 2 * b * s * h2_ * 2.5625
+        out["kv_append_prefill_175b"] = {"tokens": b * s, "h1": h2_, "avg_us": ms * 1e3,
+                                         "gbs": by / (ms / 1e3) / 1e9,
+                                         "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                         "traffic": tr.lookup("k_kv_append", "opt-175b-int4")}
+        del kv, qkv
     return out
 
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void k_quantize_g64(const uint4* __restrict__ 
     if (g < groups) {  // the same for the 8 lanes of a group
       uint32_t smw;
       const uint32_t word = quant_group8(raw[u], smw);
-      codes[g * 8 + sub] = word;
+      __builtin_nontemporal_store(word, codes + g * 8 + sub);  // streamed out
       if (sub == 0) sm[g] = smw;
     }
   }
