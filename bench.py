@@ -297,6 +297,46 @@ def quant_kernels(hp, torch, stream, c, cname, reps=10):
     return out
 
 
+def vendor_kernels(torch, stream, reps=5):
+    """Reference rates of plain torch (vendor) kernels on the same GPU, beside the
+    published peaks: a device-to-device copy of 4 GiB (read + write), a streaming sum
+    over 4 GiB of fp16 (read), and an 8192^3 fp16 product with the second operand
+    stored transposed (torch.mm on the vendor BLAS), each event-timed over `reps`
+    launches after one warm-up on seeded finite data.  They are not upper bounds:
+    several of this path's kernels run faster."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(29)
+    n = 1 << 31  # halves: 4 GiB
+    src = torch.empty(n, dtype=torch.float16, device="cuda").normal_(generator=g)
+    dst = torch.empty_like(src)
+
+    def ev_ms(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    copy_ms = ev_ms(lambda: dst.copy_(src))
+    read_ms = ev_ms(lambda: src.sum(dtype=torch.float32))
+    del dst
+    m = 8192
+    a = torch.empty((m, m), dtype=torch.float16, device="cuda").normal_(generator=g)
+    bt = torch.empty((m, m), dtype=torch.float16, device="cuda").normal_(generator=g).mul_(0.02)
+    mm_ms = ev_ms(lambda: torch.mm(a, bt.t()))
+    del src, a, bt
+    by = 2.0 * n
+    return {"copy_gbs": 2 * by / (copy_ms / 1e3) / 1e9,
+            "sum_read_gbs": by / (read_ms / 1e3) / 1e9,
+            "mm_f16_tflops": 2.0 * m ** 3 / (mm_ms / 1e3) / 1e12,
+            "work": "4 GiB device copy (read + write bytes), 4 GiB fp16 sum (read), 8192^3 "
+                    "fp16 torch.mm with the second operand transposed; reference rates of "
+                    "vendor kernels, not upper bounds"}
+
+
 def tiny_block(hp, torch, stream, reps=5):
     """The Tiny configuration (l = 2, h1 = 256, b = 4, s = 32, n = 8, int4): a whole
     block, decode columns replayed from a HIP graph against launched one kernel at a
@@ -682,6 +722,8 @@ def main():
         tree = None if args.no_tree else tree_attention(hp, torch, stream)
         log("tiny block")
         tiny = tiny_block(hp, torch, stream)
+        log("vendor kernels")
+        vend = vendor_kernels(torch, stream)
         others = {}
         if not args.no_other_configs:
             # the other OPT shapes, one block each (the timed block's buffers freed
@@ -785,6 +827,7 @@ def main():
         "quant_kernels": qk,
         "prefill_gemm_finite": dict(pgemm, block_avg_launch_ms=roof.get("avg_launch_ms")),
         "tiny_block": tiny,
+        "vendor_kernels": vend,
         "other_configs": others or None,
         "topk10_block": topk_block,
         "diagonal_block": None if diag is None else dict(
