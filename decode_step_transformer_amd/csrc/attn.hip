@@ -192,13 +192,17 @@ __device__ __forceinline__ int prefix_len(const DecArgs& a, int r) {
   return a.pos + (a.dpos ? *a.dpos : 0);
 }
 
-template <int D, bool Q4, bool MASKED>
+// A chunk of an int4 cache is 3 loads (133 VGPRs, 3 waves per SIMD: the
+// extra rows in flight outweigh the lower occupancy, 3-9% at the 30B decode
+// shape against 2 loads).  PAGED: the cache is reached through a page table
+// (one lookup per load); otherwise rows are contiguous per (request, head).
+template <int D, bool Q4, bool MASKED, bool PAGED>
 __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   using S = DecShape<D, Q4>;
   constexpr int LPR = S::LPR, RPI = S::RPI, RB = S::RB, G = S::G;
   // a chunk is U loads of RPI rows for K and for V; the next chunk is loaded
-  // while the current one is computed (int4: 118 VGPRs, 4 waves per SIMD)
-  constexpr int U = Q4 ? 2 : 4, CR = U * RPI;
+  // while the current one is computed
+  constexpr int U = Q4 ? 3 : 4, CR = U * RPI;
   const int lane = threadIdx.x;
   const int qd = lane % LPR, rho = lane / LPR;
   const int i = blockIdx.x % a.q;
@@ -207,15 +211,16 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   const int P = prefix_len(a, r);
   const int R = MASKED ? P + a.q : P + i + 1;
   const uint64_t mask = MASKED ? a.masks[(int64_t)r * a.q + i] : 0ull;
-  // wave-uniform bases, per-lane 32-bit byte offsets.  The rows of a chunk
-  // (CR rows, CR | 64 | PR) lie in one page of a paged cache: base(c) is the
-  // physical row of logical row 0 of that chunk's page, less that page's
-  // first logical row, so logical row j of the chunk is at base(c) + j.
+  // wave-uniform bases, per-lane 32-bit byte offsets.  The rows of one load
+  // (RPI rows from a multiple of RPI, RPI | 64 | PR) lie in one page of a
+  // paged cache: base(j) is the physical row of logical row j less j, so
+  // every logical row of that load is at base(j) + row (rows clamped to the
+  // last visible one stay in its page: the clamp only applies within the
+  // load that holds that row, or to loads past it, whose j is that row).
   const int64_t rowbase = ((int64_t)r * a.H + h) * a.cap;
-  auto base = [&](int c) __attribute__((always_inline)) -> int64_t {
-    if (!a.pages) return rowbase;
-    const int j = min(c * CR, R - 1);
-    return cache_row(a.pages, a.PR, a.pool, a.cap, a.H, r, h, j) - j;
+  auto base = [&](int j) __attribute__((always_inline)) -> int64_t {
+    if constexpr (!PAGED) return rowbase;
+    else return cache_row(a.pages, a.PR, a.pool, a.cap, a.H, r, h, j) - j;
   };
   const int g = Q4 ? (32 * qd) / 64 : 0;  // int4 group of this lane's dims
   const uint32_t lane_off = 16 * qd, lane_soff = 4 * g;
@@ -230,11 +235,11 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
 
   // rows past the visible range are clamped to its last row (their weight is 0)
   auto load = [&](DecPart<U, Q4>& X, const void* cache, const uint32_t* smc, int c) {
-    const int64_t b0 = base(c);
-    const uint8_t* cb = (const uint8_t*)cache + b0 * RB;
-    const uint8_t* sb = (const uint8_t*)(smc + b0 * G);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int64_t bu = base(min(c * CR + RPI * u, R - 1));
+      const uint8_t* cb = (const uint8_t*)cache + bu * RB;
+      const uint8_t* sb = (const uint8_t*)(smc + bu * G);
       const uint32_t row = (uint32_t)min(c * CR + rho + RPI * u, R - 1);
       // the cache is streamed once per step: non-temporal loads keep it from
       // displacing reusable lines in the caches
@@ -698,14 +703,23 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
   const dim3 grid((unsigned)((int64_t)b * heads * q));
   Prof prof(kv.fmt == HP_Q4 ? "attn_decode_q4" : "attn_decode_f16", st);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, a); };
-  const bool m = masks != nullptr, q4 = kv.fmt == HP_Q4;
-  if (D == 128) {
-    if (q4) m ? go(k_decode_attn<128, true, true>) : go(k_decode_attn<128, true, false>);
-    else m ? go(k_decode_attn<128, false, true>) : go(k_decode_attn<128, false, false>);
-  } else {
-    if (q4) m ? go(k_decode_attn<64, true, true>) : go(k_decode_attn<64, true, false>);
-    else m ? go(k_decode_attn<64, false, true>) : go(k_decode_attn<64, false, false>);
-  }
+  const bool m = masks != nullptr, q4 = kv.fmt == HP_Q4, paged = a.pages != nullptr;
+  auto pick = [&](auto d_, auto q4_) {
+    constexpr int Dd = decltype(d_)::value;
+    constexpr bool Qq = decltype(q4_)::value;
+    if (paged)
+      m ? go(k_decode_attn<Dd, Qq, true, true>) : go(k_decode_attn<Dd, Qq, false, true>);
+    else
+      m ? go(k_decode_attn<Dd, Qq, true, false>) : go(k_decode_attn<Dd, Qq, false, false>);
+  };
+  using I128 = std::integral_constant<int, 128>;
+  using I64 = std::integral_constant<int, 64>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (D == 128)
+    q4 ? pick(I128(), T_()) : pick(I128(), F_());
+  else
+    q4 ? pick(I64(), T_()) : pick(I64(), F_());
 }
 
 void launch_prefill_attention(int32_t b, int32_t s, int32_t h1, int32_t heads, const void* qkv,
