@@ -22,16 +22,17 @@
 namespace hp {
 
 // ------------------------------------------------------------ KV append
-// A workgroup codes 32 AU groups of 64 channels of one new token's K | V
-// columns (2 h1 contiguous halves: a wave reads 1 KB contiguous; a lane codes
-// AU groups, their loads issued first) and writes each group into the
-// head-major cache row of its head.  Neighbouring rows of one head share
-// cache lines, so the workgroups of TQ consecutive tokens (TQ = 16: 1 KB of
-// codes and 128 B of scale/min pairs per head) are given ids of one residue
-// mod 8: workgroup ids reach the 8 XCDs round-robin, so those rows are all
-// written through one XCD's L2, which gathers the pieces of each line before
-// writing it back (with consecutive ids, neighbouring rows came through
-// different L2s and reached HBM as partial lines).
+// Per-token form (decode steps, ragged or paged appends, d = 64, fp16
+// caches; whole 16-row chunks of a contiguous int4 cache with d = 128 go to
+// k_kv_append_tile below): a workgroup codes 32 AU groups of 64 channels of
+// one new token's K | V columns (2 h1 contiguous halves: a wave reads 1 KB
+// contiguous; a lane codes AU groups, their loads issued first) and writes
+// each group into the head-major cache row of its head.  Neighbouring rows of
+// one head share cache lines, so the workgroups of 16 consecutive tokens are
+// given ids of one residue mod 8 (workgroup ids reach the 8 XCDs round-robin)
+// and write those lines through one XCD's L2.  Their 8-byte scale/min pieces
+// still reach memory as partial writes (1.3x the written bytes at the
+// prefill shapes), which is what the tiled form avoids.
 struct AppendArgs {
   const _Float16* qkv;
   int b, q, h1, H, D, pos;
