@@ -29,6 +29,9 @@ Prints one JSON line (rank 0, N = 1 only):
   tree_attention-- the tree-masked decode attention workload (8 requests,
                    2048-row int4 prefix, 64 tree tokens), event-timed, with the
                    pruning plan and cache compaction after verification;
+  achievable    -- the rates the library's probes attain on this GPU (a
+                   streaming read, independent MFMA chains); the roofline
+                   reports its fraction of those beside the published peak;
   cpu_baseline  -- the CPU oracle timed on a bounded sample of the same
                    workload (one decode layer for a few requests).
 """
@@ -295,6 +298,40 @@ def quant_kernels(hp, torch, stream, c, cname, reps=10):
                                          "traffic": tr.lookup("k_kv_append", "opt-175b-int4")}
         del kv, qkv
     return out
+
+
+def achievable(hp, torch, stream, reps=5):
+    """What this GPU attains on the two resources the kernels are bound by,
+    measured with the library's own probes (hp_peak_read, hp_peak_mfma): a
+    streaming read of 4 GiB (16-byte non-temporal loads, 8 workgroups per CU)
+    and independent 16x16x32 fp16 MFMA chains on two waves per SIMD of every
+    CU, each event-timed over `reps` launches after one warm-up."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31)
+    x = torch.empty(1 << 31, dtype=torch.float16, device="cuda").normal_(generator=g)
+    sink = torch.zeros(8 * 8 * cus, dtype=torch.int32, device="cuda")
+
+    def ev_ms(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    read_ms = ev_ms(lambda: hp.hp_peak_read(x, 8 * cus, sink, stream=stream))
+    iters = 20000
+    mfma_ms = ev_ms(lambda: hp.hp_peak_mfma(iters, cus, sink, stream=stream))
+    nbytes = x.numel() * 2
+    del x, sink
+    return {"hbm_read_gbs": nbytes / (read_ms / 1e3) / 1e9,
+            "mfma_f16_tflops": cus * 8 * 16 * iters * 16384 / (mfma_ms / 1e3) / 1e12,
+            "cus": cus,
+            "work": "hp_peak_read over 4 GiB; hp_peak_mfma: 16 independent 16x16x32 fp16 "
+                    "MFMA chains per wave, 8 waves per CU, 20000 rounds"}
 
 
 def vendor_kernels(torch, stream, reps=5):
@@ -724,6 +761,8 @@ def main():
         tiny = tiny_block(hp, torch, stream)
         log("vendor kernels")
         vend = vendor_kernels(torch, stream)
+        log("achievable peaks")
+        ach = achievable(hp, torch, stream)
         others = {}
         if not args.no_other_configs:
             # the other OPT shapes, one block each (the timed block's buffers freed
@@ -762,6 +801,9 @@ def main():
         roof = {"kernel": name, "bound": None, "achieved": None, "peak": None, "unit": None,
                 "frac": None, "traffic": None, "launches": launches,
                 "avg_launch_ms": tot_ms / launches}
+    if roof.get("bound") == "mfma":
+        roof["achievable_peak"] = ach["mfma_f16_tflops"]
+        roof["frac_of_achievable"] = roof["achieved"] / ach["mfma_f16_tflops"]
 
     # decode-phase kernels
     dec = {}
@@ -828,6 +870,7 @@ def main():
         "prefill_gemm_finite": dict(pgemm, block_avg_launch_ms=roof.get("avg_launch_ms")),
         "tiny_block": tiny,
         "vendor_kernels": vend,
+        "achievable": ach,
         "other_configs": others or None,
         "topk10_block": topk_block,
         "diagonal_block": None if diag is None else dict(

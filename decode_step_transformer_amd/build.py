@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libhp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["quant.hip", "gemm.hip", "gemm_dec.hip", "gemm16.hip", "attn.hip", "tree.hip", "topk.hip",
-           "layer.hip"]
+           "layer.hip", "peaks.hip"]
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

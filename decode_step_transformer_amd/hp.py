@@ -61,6 +61,7 @@ EXPORTS = [
     "hp_workspace_bytes", "hp_layer_prefill", "hp_layer_decode", "hp_run_block",
     "hp_release_graphs", "hp_weight_bytes", "hp_kv_bytes", "hp_profile", "hp_profile_read",
     "hp_debug_set_capture", "hp_kv_append_ragged", "hp_diagonal_pages",
+    "hp_peak_read", "hp_peak_mfma",
 ]
 
 _lib = None
@@ -99,6 +100,8 @@ def lib():
                                 C.POINTER(hp_kv), _p, _p, _sz, _p],
             "hp_run_block": [C.POINTER(hp_dims), C.POINTER(hp_layer), _p, _p, C.POINTER(hp_kv), _p,
                              _p, _p, _sz, C.c_uint32, C.POINTER(C.c_float), _p],
+            "hp_peak_read": [_p, C.c_uint64, _i32, _p, _p],
+            "hp_peak_mfma": [_i32, _i32, _p, _p],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -439,6 +442,17 @@ def hp_kv_bytes(d: hp_dims, fmt: int) -> int:
 # ---------------------------------------------------------------- profiling
 def hp_profile(on: bool):
     lib().hp_profile(1 if on else 0)
+
+
+def hp_peak_read(x: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None):
+    """Streams x once (a measurement probe, see include/hp.h)."""
+    _check(lib().hp_peak_read(_ptr(x), x.numel() * x.element_size(), workgroups, _ptr(sink),
+                              _stream(stream)))
+
+
+def hp_peak_mfma(iters: int, workgroups: int, sink: torch.Tensor, stream=None):
+    """8 * 16 * iters fp16 16x16x32 MFMAs per workgroup (a measurement probe)."""
+    _check(lib().hp_peak_mfma(iters, workgroups, _ptr(sink), _stream(stream)))
 
 
 def hp_profile_read() -> dict:

@@ -415,6 +415,23 @@ void hp_release_graphs(void);
 int32_t hp_profile(int32_t on);
 int32_t hp_profile_read(char* buf, size_t len);
 
+/* ---------------------------------------------------- achievable peaks */
+/* Measurement probes, not part of the layer: the rates this GPU attains on
+ * the two resources the kernels are bound by, the reference for their
+ * fractions beside the published peaks.  hp_peak_read streams `bytes` bytes
+ * of the device buffer x once (16-byte non-temporal loads; x and bytes
+ * multiples of 16) over `workgroups` workgroups of 256 threads.
+ * hp_peak_mfma runs `iters` rounds of 16 independent
+ * v_mfma_f32_16x16x32_f16 (16 x 16 x 32 fp16 products, 16384 flop each) in
+ * each of the 8 waves of `workgroups` workgroups of 512 threads (operand
+ * values arbitrary): 8 * 16 * iters * 16384 flop per workgroup.  sink:
+ * device uint32, at least workgroups (read) or 8 * workgroups (mfma) words,
+ * contents meaningless.  Both enqueue on `stream` (time them with events)
+ * and return HP_ERR_NULL / HP_ERR_SHAPE for bad arguments. */
+hp_status hp_peak_read(const void* x, uint64_t bytes, int32_t workgroups, uint32_t* sink,
+                       void* stream);
+hp_status hp_peak_mfma(int32_t iters, int32_t workgroups, uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------ sizes */
 /* [FlexGen] background section (memory bottleneck analysis): weight bytes
  * l(8 h1^2 + 4 h1 h2) in fp16, and peak KV bytes 4 b l h1 (s + n) in fp16;

@@ -125,3 +125,16 @@ def test_diagonal_pages():
     paged = hp.hp_diagonal_pages(d, 64) * 64
     assert 0.5 < paged / full < 0.6
     assert hp.hp_diagonal_pages(d, 48) == 0            # page rows must be a multiple of 64
+
+
+def test_peak_probes_reject_bad_arguments_on_the_host():
+    """The measurement probes check their arguments before any launch."""
+    import ctypes as C
+    from decode_step_transformer_amd import hp
+    L = hp.lib()
+    assert L.hp_peak_read(None, 1024, 8, C.c_void_p(16), None) == -1
+    assert L.hp_peak_read(C.c_void_p(16), 1000, 8, C.c_void_p(16), None) == -2  # bytes % 16
+    assert L.hp_peak_read(C.c_void_p(8), 1024, 8, C.c_void_p(16), None) == -2   # x % 16
+    assert L.hp_peak_read(C.c_void_p(16), 1024, 0, C.c_void_p(16), None) == -2
+    assert L.hp_peak_mfma(10, 8, None, None) == -1
+    assert L.hp_peak_mfma(0, 8, C.c_void_p(16), None) == -2

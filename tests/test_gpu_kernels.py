@@ -253,3 +253,29 @@ def test_tree_masks(hp, orc):
     masks, err = hp.hp_tree_masks(dev(bad.astype(np.int32)))
     assert int(host(err)[0]) == 2
     assert int(host(masks).view(np.uint64)[0, 5]) == 1 << 5
+
+
+def test_peak_probes_run(hp):
+    """The measurement probes run and report rates in the range of the hardware
+    (loose floors: a stream of 1 GiB above 2 TB/s, MFMA chains above 0.8 PFLOP/s)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    x = torch.ones(1 << 29, dtype=torch.float16, device="cuda")
+    sink = torch.zeros(64 * cus, dtype=torch.int32, device="cuda")
+
+    def ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 3
+
+    t_read = ms(lambda: hp.hp_peak_read(x, 8 * cus, sink))
+    assert (1 << 30) / (t_read / 1e3) > 2e12
+    t_mfma = ms(lambda: hp.hp_peak_mfma(2000, cus, sink))
+    assert cus * 8 * 16 * 2000 * 16384 / (t_mfma / 1e3) > 0.8e15
+    assert not sink.any()  # the probes' folded values never match their store condition
