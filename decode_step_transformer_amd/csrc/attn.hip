@@ -344,8 +344,10 @@ __device__ __forceinline__ int swz_v(int key) {
 
 // One block of 64 keys for the 16 queries of a wave (query l % 16 per lane):
 // scores S^T = K Q^T, keys with !visible(kidx) masked, online softmax, and
-// O^T += V^T P^T.  Kl, Vl: fp16 tiles of the block (64 rows of 2 D bytes).
-template <int D, class Vis>
+// O^T += V^T P^T.  Kl, Vl: fp16 tiles of the block (64 rows of 2 D bytes);
+// VK: the V tile uses the K tile's chunk swizzle (the transposing reads
+// measured as fast with either).
+template <int D, bool VK = false, class Vis>
 __device__ __forceinline__ void flash_block(const uint8_t* Kl, const uint8_t* Vl,
                                             const f16x8 (&qf)[D / 32], int k0, Vis visible,
                                             float c2, float& m_run, float& l_lane,
@@ -407,7 +409,7 @@ __device__ __forceinline__ void flash_block(const uint8_t* Kl, const uint8_t* Vl
       for (int n2 = 0; n2 < 2; ++n2) {
         const int row = 32 * p + 8 * G + 4 * n2 + r16 / 4;
         const int d = 16 * db + 4 * (r16 % 4);
-        const uint8_t* vp = Vl + row * RB + 16 * ((d / 8) ^ swz_v<SPR>(row)) + 2 * (d % 8);
+        const uint8_t* vp = Vl + row * RB + 16 * ((d / 8) ^ (VK ? swz_k<SPR>(row) : swz_v<SPR>(row))) + 2 * (d % 8);
         const f16x4 th = __builtin_bit_cast(f16x4, ds_read_tr16(vp));
 #pragma unroll
         for (int e = 0; e < 4; ++e) vf[4 * n2 + e] = th[e];
@@ -417,21 +419,31 @@ __device__ __forceinline__ void flash_block(const uint8_t* Kl, const uint8_t* Vl
   }
 }
 
-// Normalised output of a wave's 16 queries: lane l holds dims 16 db + 4 (l / 16) + e.
-template <int D>
+// Normalised output of a wave's 16 queries: lane l holds tile positions
+// 16 db + 4 (l / 16) + e.  PERM: the V tile stores each 8-dim chunk in the
+// order 0 4 1 5 2 6 3 7 (the int4 expansion's natural order), so a lane with
+// l / 16 even holds dims {0, 4, 1, 5} of its chunk and the lane 16 above it
+// dims {2, 6, 3, 7}; the pair swaps two values to write dims in order.
+template <int D, bool PERM = false>
 __device__ __forceinline__ void flash_store(_Float16* row, float l_lane, const f32x4 (&o)[D / 16]) {
   const int G = (threadIdx.x & 63) >> 4;
   // the 4 lanes of a query hold complementary key subsets: total their sums
   float l = l_lane + __shfl_xor(l_lane, 16);
   l += __shfl_xor(l, 32);
-  if (!row) return;
   const float inv = 1.0f / l;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
     f16x4 y;
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[db][e] * inv);
-    *(f16x4*)(row + 16 * db + 4 * G) = y;
+    if constexpr (PERM) {
+      // even G sends dims 4, 5 (y1, y3) and receives 2, 3; odd G the reverse
+      const bool odd = G & 1;
+      const f16x2 send = odd ? f16x2{y[0], y[2]} : f16x2{y[1], y[3]};
+      const f16x2 got = h2_of(__shfl_xor(__builtin_bit_cast(uint32_t, send), 16));
+      y = odd ? f16x4{got[0], got[1], y[1], y[3]} : f16x4{y[0], y[2], got[0], got[1]};
+    }
+    if (row) *(f16x4*)(row + 16 * db + 4 * G) = y;
   }
 }
 
@@ -560,15 +572,27 @@ __global__ __launch_bounds__(256, 2) void k_multi_attn(DecArgs a) {
   const uint32_t* ks_ = a.ksm + rowbase * NG;
   const uint32_t* vs_ = a.vsm + rowbase * NG;
 
+  // Q fragments in the tiles' dim order (each 8-dim chunk as 0 4 1 5 2 6 3 7)
   f16x8 qf[KS];
   {
     const _Float16* qp = a.qkv + ((int64_t)r * a.q + qrow) * 3 * a.h1 + h * D + 8 * G;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) qf[k] = *(const f16x8*)(qp + 32 * k);
+    for (int k = 0; k < KS; ++k) {
+      const f16x8 v = *(const f16x8*)(qp + 32 * k);
+      qf[k] = f16x8{v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};
+    }
   }
 
   // this wave's units of a block: rows 16 wave .. 16 wave + 15 of K and V,
   // unit u = 64 p + lane -> tensor, row, 16-byte piece
+  // unit rem of a tensor: row and 16-byte piece.  With 4 pieces per row,
+  // 16 consecutive lanes take pieces 0..3 of 4 consecutive rows (4 rows per
+  // piece), so each 8-lane group of a tile write covers 4 rows x 2 pieces:
+  // with the K swizzle (used for both tiles here) their 16-byte slots fall in
+  // distinct banks.  Rows 0..3 x pieces 0..3 are still one contiguous 256 B
+  // of the cache for the loads.
+  auto urow = [](int rem) { return PPR == 4 ? (rem & 3) + 4 * (rem >> 4) : rem / PPR; };
+  auto upiece = [](int rem) { return PPR == 4 ? (rem >> 2) & 3 : rem % PPR; };
   struct Codes {
     u32x4 w[NP];
     uint32_t sm[NP];
@@ -578,33 +602,41 @@ __global__ __launch_bounds__(256, 2) void k_multi_attn(DecArgs a) {
     for (int p = 0; p < NP; ++p) {
       const int u = 64 * p + lane;
       const int tsr = u / (16 * PPR), rem = u % (16 * PPR);
-      const int row = min(kb * 64 + 16 * wave + rem / PPR, R - 1), piece = rem % PPR;
+      const int row = min(kb * 64 + 16 * wave + urow(rem), R - 1), piece = upiece(rem);
       C.w[p] = __builtin_nontemporal_load(
           (const u32x4*)((tsr ? vc : kc) + (int64_t)row * CB + 16 * piece));
       C.sm[p] = (tsr ? vs_ : ks_)[(int64_t)row * NG + (32 * piece) / 64];
     }
   };
-  const uint32_t magic = in_vgpr(0x54006400u);
-  const f16x2 off = {(_Float16)-1024.0f, (_Float16)-64.0f};
+  // A code dword holds dims 0..7 of its piece (low nibble first).  Masking it
+  // and its 8-bit shift into the exponents of 1024 and 64 gives the pairs
+  // (0, 4), (1, 5), (2, 6), (3, 7) with no byte permute, so every 8-dim
+  // chunk of the tiles is stored in that order (Q is loaded in the same
+  // order, and the output is put back in flash_store).
+  const uint32_t m_lo = in_vgpr(0x64006400u), m_hi = in_vgpr(0x54005400u);
+  const f16x2 off_lo = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const f16x2 off_hi = {(_Float16)-64.0f, (_Float16)-64.0f};
   auto expand = [&](const Codes& C, uint8_t* tl) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int u = 64 * p + lane;
       const int tsr = u / (16 * PPR), rem = u % (16 * PPR);
-      const int row = 16 * wave + rem / PPR, piece = rem % PPR;
-      const int swz = tsr ? swz_v<SPR>(row) : swz_k<SPR>(row);
+      const int row = 16 * wave + urow(rem), piece = upiece(rem);
+      const int swz = swz_k<SPR>(row);
       uint8_t* dst_row = tl + tsr * 64 * RB + row * RB;
       const f16x2 sm = h2_of(C.sm[p]);
       const f16x2 sc = {sm[0], sm[0]}, mn = {sm[1], sm[1]};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const uint32_t w = C.w[p][j], w8 = w >> 8;
+        const f16x2 c[4] = {h2_of((w & 0x000F000Fu) | m_lo) + off_lo,
+                            h2_of((w & 0x00F000F0u) | m_hi) + off_hi,
+                            h2_of((w8 & 0x000F000Fu) | m_lo) + off_lo,
+                            h2_of((w8 & 0x00F000F0u) | m_hi) + off_hi};
         u32x4 y;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t x = __builtin_amdgcn_perm(C.w[p][j], C.w[p][j], 0x0C000C00u | q | (q << 16));
-          const f16x2 c = h2_of((x & 0x00F0000Fu) | magic) + off;
-          y[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, sc, mn));
-        }
+        for (int q = 0; q < 4; ++q)
+          y[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c[q], sc, mn));
         *(u32x4*)(dst_row + 16 * ((4 * piece + j) ^ swz)) = y;
       }
     }
@@ -637,7 +669,7 @@ __global__ __launch_bounds__(256, 2) void k_multi_attn(DecArgs a) {
       __attribute__((always_inline)) {
     load(Cfree, min(kb + 2, nkb - 1));
     expand(Cnext, tnext);
-    flash_block<D>(tcur, tcur + 64 * RB, qf, kb * 64, vis, c2, m_run, l_lane, o);
+    flash_block<D, true>(tcur, tcur + 64 * RB, qf, kb * 64, vis, c2, m_run, l_lane, o);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();  // tnext complete; every wave is done with tcur
   };
@@ -660,7 +692,7 @@ __global__ __launch_bounds__(256, 2) void k_multi_attn(DecArgs a) {
       if (kb + 1 < nkb) iter(kb + 1, C0, C1, tiles + TILE, tiles, visible);
     }
   }
-  flash_store<D>(qi < a.q ? a.out + ((int64_t)r * a.q + qi) * a.h1 + h * D : nullptr, l_lane, o);
+  flash_store<D, true>(qi < a.q ? a.out + ((int64_t)r * a.q + qi) * a.h1 + h * D : nullptr, l_lane, o);
 }
 
 // -------------------------------------------------------------- launchers

@@ -22,7 +22,7 @@
 //    subtile and one dword of scales/mins per lane; the 8 scale and 8 min
 //    pairs a lane needs per k-step come from the lanes of its row of 16 by
 //    DPP broadcast.  Activation rows are 256 B with 16-byte chunks XOR-
-//    swizzled by row (fragment reads of 16 rows hit distinct banks).
+//    swizzled by row (a fragment read hits every bank once).
 //  * Codes are expanded in registers with the magic-exponent trick and one
 //    packed FMA with scale and min (a single rounding).
 //  * Split partials go to fp32 scratch in the kernel's own tile-major order
@@ -66,6 +66,14 @@ struct DqArgs {
   int64_t ldy;
   float* P;  // split partials [split][M][N] or null
 };
+
+// Chunk swizzle of an activation row r (16-byte chunk c sits in slot
+// c ^ xswz(r & 15)): a fragment read puts 16 rows x 4 lane quarters of
+// chunks on LDS banks; with the bits of r reordered, the rows of one parity
+// use one of each pair of slots {x, x ^ 4}, so lane quarters 0 and 1 (and 2
+// and 3) never meet in a bank (the plain r ^ c put them 2-way in conflict,
+// measured with SQ_LDS_BANK_CONFLICT).
+__device__ __forceinline__ int xswz(int r) { return ((r >> 1) & 3) | ((r & 1) << 2) | (r & 8); }
 
 // Lane n of each row of 16 lanes, to every lane of that row.
 template <int n>
@@ -113,7 +121,7 @@ __device__ __forceinline__ void dq_pair(const DqArgs& g, uint8_t* lds, int wave,
   // last one).  Chunk `wave` of the 8 scale / min chunks: the scales (even)
   // or mins (odd) of group wave >> 1.
   const int r0 = 4 * wave + (lane >> 4);
-  const int cx = (lane & 15) ^ (r0 & 15);
+  const int cx = (lane & 15) ^ xswz(r0 & 15);
   const uint32_t xoff = (uint32_t)(r0 * g.lda + 8 * cx) * 2u;
   const uint32_t xoff_last =
       (uint32_t)((min(32 * (NX - 1) + r0, g.M - 1) - 32 * (NX - 1)) * g.lda + 8 * cx) * 2u;
@@ -154,7 +162,7 @@ __device__ __forceinline__ void dq_pair(const DqArgs& g, uint8_t* lds, int wave,
   // k-step j of a k-block: lane quarter kq covers k = 32 kq + 8 j .. +7
   auto read_x = [&](f16x8& o, int xs, auto j_, int i) __attribute__((always_inline)) {
     constexpr int j = decltype(j_)::value;
-    o = *(const f16x8*)(Xl + xs * XB + (16 * i + r16) * 256 + 16 * ((4 * kq + j) ^ r16));
+    o = *(const f16x8*)(Xl + xs * XB + (16 * i + r16) * 256 + 16 * ((4 * kq + j) ^ xswz(r16)));
   };
   // Codes: dwords J0, J0 + 1 of the lane's 16 bytes.  Scales: the lane
   // quarter's 16 k (32 kq + 8 J0 ..) need 8 scale and 8 min dwords; lane d
