@@ -73,8 +73,9 @@ hp_status launch_gemm_dq(const void* x, int64_t ldx, const hp_mat& w, int64_t M,
                          int64_t ldr, bool relu, void* y, int64_t ldy, int splits, float* partials,
                          hipStream_t st);
 
-// fp16 tiled product for tall M (wt = [n][k] fp16) and the int4 -> fp16
-// weight expansion that feeds it.
+// fp16 tiled product for tall M and the int4 -> fp16 weight expansion that
+// feeds it.  ldw == 0: wt is in the fragment-major HP_F16 layout; else wt =
+// [n][k] fp16 rows of stride ldw (the expansion's output).
 hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int64_t ldw, int k, int n,
                         int64_t M, const void* res, int64_t ldr, bool relu, void* y, int64_t ldy,
                         hipStream_t st);

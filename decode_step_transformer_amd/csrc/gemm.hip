@@ -11,11 +11,13 @@
 //    registers (48 VGPRs) and a CU holds up to 16 waves.
 //  * The activation tile x[BM][128] of each k-block is staged through LDS
 //    (three stages, rows padded by 16 B) and shared by the 8 waves.
-//  * Weight fragments (fp16, wt[n][k] rows) go straight from HBM to
-//    registers, four 16-byte chunks per lane and subtile per k-block.  The
-//    k-steps keep the operand layout's natural order (k-step j of a block is
-//    k = 32 j .. 32 j + 31, lane quarter q holding 32 j + 8 q .. + 7), so
-//    each load instruction reads 64 contiguous bytes from each of 16 rows.
+//  * Weight fragments go straight from HBM to registers, four 16-byte chunks
+//    per lane and subtile per k-block.  The fp16 weight layout is fragment-
+//    major (k-step j of a block is k = 32 j .. 32 j + 31, lane quarter q
+//    holding 32 j + 8 q .. + 7, and the 64 lanes' fragments are contiguous),
+//    so each load instruction reads one contiguous 1 KB; with rows of w^T
+//    instead (16 rows x 64 bytes per instruction, rows a power-of-two apart)
+//    the products ran 8-21% slower.
 //  * MFMA operand A is the weight fragment (16 output columns), operand B the
 //    activation fragment (16 rows), so each lane ends with 4 consecutive
 //    output columns of one row: 8-byte stores.
@@ -129,12 +131,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, _Float16* As_, int 
   struct Raw {
     u32x4 c[4];  // the 4 k-steps of one k-block
   };
-  const _Float16* Bh = g.B + (int64_t)(n_ld + r16) * g.K + 8 * kq;
+  // fragment-major weight tiles (4 KB per 16 columns x 128 inputs): k-step j
+  // of block kb is one contiguous 1 KB, lane L's 16 bytes at L * 16
+  const _Float16* Bh = g.B + ((int64_t)(n_ld / 16) * KB * 256 + lane) * 8;
   auto load_b = [&](Raw& R, int kb) __attribute__((always_inline)) {
-    const u32x4* p = (const u32x4*)(Bh + (int64_t)kb * BK);
+    const u32x4* p = (const u32x4*)(Bh + (int64_t)kb * 2048);
     unroll<4>([&](auto j_) {
       constexpr int j = decltype(j_)::value;
-      R.c[j] = p[4 * j];
+      R.c[j] = p[64 * j];
     });
   };
 
@@ -456,7 +460,7 @@ hp_status launch_gemm(const void* x, int64_t ldx, const hp_mat& w, int64_t M, co
     if (s != HP_OK) return s;
     return launch_gemm16(x, ldx, ws, pad_ld(w.k), w.k, w.n, M, res, ldr, relu, y, ldy, st);
   }
-  return launch_gemm16(x, ldx, w.data, w.k, w.k, w.n, M, res, ldr, relu, y, ldy, st);
+  return launch_gemm16(x, ldx, w.data, 0, w.k, w.n, M, res, ldr, relu, y, ldy, st);
 }
 
 }  // namespace hp

@@ -43,7 +43,7 @@ __device__ __forceinline__ void unroll16(F&& f) {
 struct G16Args {
   const _Float16* A;
   int64_t lda, M;
-  const _Float16* W;  // wt[N][K], row stride ldw
+  const _Float16* W;  // FRAG: fragment-major tiles; else wt[N][K], row stride ldw
   int64_t ldw;
   int K, N, mtiles, ntiles;
   const _Float16* res;
@@ -53,6 +53,11 @@ struct G16Args {
   int64_t ldy;
 };
 
+// FRAG: the weight is in the fragment-major HP_F16 layout (tile of 16
+// columns x 128 inputs = 4 KB, k-step j's 1 KB holding lane L's 8 inputs
+// 32 j + 8 (L / 16) .. of column L % 16); else rows wt[n][k] (the int4
+// expansion).  Either way a direct load fills the same LDS image.
+template <bool FRAG>
 __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
   __shared__ __attribute__((aligned(1024))) _Float16 S[G_NS * G_STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -88,19 +93,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
   for (int h = 0; h < 2; ++h) {
     const int64_t m = min(m0 + 16 * (2 * wave + h) + rin, g.M - 1);
     srcA[h] = g.A + m * g.lda + 8 * cchunk;
-    const int64_t n = min(n0 + 16 * (2 * wave + h) + rin, g.N - 1);
-    srcB[h] = g.W + n * g.ldw + 8 * cchunk;
+    if constexpr (FRAG) {
+      const int64_t nb = min(n0 + 16 * (2 * wave + h), g.N - 16) / 16;
+      srcB[h] = g.W + nb * (g.K / 128) * 2048 + (rin + 16 * cchunk) * 8;
+    } else {
+      const int64_t n = min(n0 + 16 * (2 * wave + h) + rin, g.N - 1);
+      srcB[h] = g.W + n * g.ldw + 8 * cchunk;
+    }
   }
   const uint32_t sbase = lds_off(S);
   auto issue = [&](int ks, int stage) __attribute__((always_inline)) {
-    const int64_t ko = (int64_t)ks * G_BK;
+    const int64_t ko = (int64_t)ks * G_BK, kob = FRAG ? (int64_t)ks * 512 : ko;
     const uint32_t st = sbase + (uint32_t)stage * G_STAGE * 2;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       dma16(srcA[h] + ko, __builtin_amdgcn_readfirstlane(st + (2 * wave + h) * 1024));
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      dma16(srcB[h] + ko, __builtin_amdgcn_readfirstlane(st + G_BM * 64 + (2 * wave + h) * 1024));
+      dma16(srcB[h] + kob, __builtin_amdgcn_readfirstlane(st + G_BM * 64 + (2 * wave + h) * 1024));
   };
 
   f16x8 fa[2][8], fb[2][4];
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
     wait_vm<8, 0>();  // this wave's reads of stage kk are done, and its loads of kk+1
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t ko = (int64_t)ck(kk + 4) * G_BK;
+    const int64_t ko = (int64_t)ck(kk + 4) * G_BK, kob = FRAG ? (int64_t)ck(kk + 4) * 512 : ko;
     const uint32_t stg = sbase + (uint32_t)(kk & 3) * G_STAGE * 2;
     const _Float16* St = S + ((kk + 1) & 3) * G_STAGE;
     const int slot = (kq ^ ((r16 >> 1) & 3)) * 8;
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
       if constexpr (c < 2)
         dma16(srcA[c] + ko, __builtin_amdgcn_readfirstlane(stg + (2 * wave + c) * 1024));
       else
-        dma16(srcB[c - 2] + ko,
+        dma16(srcB[c - 2] + kob,
               __builtin_amdgcn_readfirstlane(stg + G_BM * 64 + (2 * wave + c - 2) * 1024));
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -264,7 +274,11 @@ hp_status launch_gemm16(const void* x, int64_t ldx, const void* wt, int64_t ldw,
   a.Y = (_Float16*)y;
   a.ldy = ldy;
   Prof prof("gemm_f16_tiled", st);
-  hipLaunchKernelGGL(k_gemm16, dim3((unsigned)(a.mtiles * a.ntiles)), dim3(512), 0, st, a);
+  const dim3 grid((unsigned)(a.mtiles * a.ntiles));
+  if (ldw == 0)
+    hipLaunchKernelGGL(k_gemm16<true>, grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_gemm16<false>, grid, dim3(512), 0, st, a);
   return launch_ok("k_gemm16");
 }
 

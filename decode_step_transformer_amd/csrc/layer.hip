@@ -494,12 +494,13 @@ hp_status hp_pack_weight_q4(const void* codes, const void* sm, int32_t k, int32_
 }
 
 hp_status hp_pack_weight_f16(const void* w, int32_t k, int32_t n, void* wt, void* stream) {
-  if (k <= 0 || n <= 0) return fail(HP_ERR_SHAPE, "k, n must be positive");
+  if (k <= 0 || n <= 0 || k % 128 || n % 64) return fail(HP_ERR_SHAPE, "need k %% 128 == 0, n %% 64 == 0");
   if (!w || !wt) return fail(HP_ERR_NULL, "NULL pointer");
+  NEED_ALIGN(wt, 16);
   hp_status s = device_check();
   if (s != HP_OK) return s;
   launch_pack_f16(w, k, n, wt, S(stream));
-  return launch_ok("k_transpose_f16");
+  return launch_ok("k_pack_f16");
 }
 
 size_t hp_gemm_workspace_bytes(int64_t M, int32_t k, int32_t n, int32_t fmt) {

@@ -103,19 +103,31 @@ __global__ __launch_bounds__(256) void k_pack_sm(const uint32_t* __restrict__ sm
   }
 }
 
-// fp16 w[k][n] -> wt[n][k], 64x64 tiles through LDS.
-__global__ __launch_bounds__(256) void k_transpose_f16(const uint16_t* __restrict__ w, int32_t k,
-                                                       int32_t n, uint16_t* __restrict__ wt) {
+// fp16 w[k][n] -> the fragment-major HP_F16 layout: tile (nb, kb) of 16
+// output columns x 128 inputs is 4 KB contiguous, [j][lane][8] halves, lane
+// L holding column 16 nb + L % 16 at inputs 128 kb + 32 j + 8 (L / 16) + e
+// (exactly one MFMA operand fragment per k-step j).  64 x 64 tiles of w pass
+// through LDS; each thread writes 8 consecutive inputs of one column (16 B).
+__global__ __launch_bounds__(256) void k_pack_f16(const uint16_t* __restrict__ w, int32_t k,
+                                                  int32_t n, uint16_t* __restrict__ wt) {
   __shared__ uint16_t tile[64][65];
   const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int r = i / 64, c = i % 64;
-    if (k0 + r < k && n0 + c < n) tile[r][c] = w[(int64_t)(k0 + r) * n + n0 + c];
+    tile[r][c] = w[(int64_t)(k0 + r) * n + n0 + c];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int r = i / 64, c = i % 64;  // r: n offset, c: k offset
-    if (n0 + r < n && k0 + c < k) wt[(int64_t)(n0 + r) * k + k0 + c] = tile[c][r];
+  const int64_t KB = k / 128;
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int c = i / 8, k8 = (i % 8) * 8;  // column n0 + c, inputs k0 + k8 .. + 7
+    const int nn = n0 + c, kk = k0 + k8;
+    const int64_t off = (((int64_t)(nn / 16) * KB + kk / 128) * 4 + (kk % 128) / 32) * 512 +
+                        ((nn % 16) + 16 * ((kk % 32) / 8)) * 8;
+    uint32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = (uint32_t)tile[k8 + 2 * e][c] | ((uint32_t)tile[k8 + 2 * e + 1][c] << 16);
+    *(uint4*)(wt + off) = uint4{v[0], v[1], v[2], v[3]};
   }
 }
 
@@ -152,8 +164,8 @@ void launch_pack_q4(const void* codes, const void* sm, int32_t k, int32_t n, voi
 }
 
 void launch_pack_f16(const void* w, int32_t k, int32_t n, void* wt, hipStream_t st) {
-  hipLaunchKernelGGL(k_transpose_f16, dim3((unsigned)cdiv(n, 64), (unsigned)cdiv(k, 64)),
-                     dim3(256), 0, st, (const uint16_t*)w, k, n, (uint16_t*)wt);
+  hipLaunchKernelGGL(k_pack_f16, dim3((unsigned)(n / 64), (unsigned)(k / 64)), dim3(256), 0, st,
+                     (const uint16_t*)w, k, n, (uint16_t*)wt);
 }
 
 }  // namespace hp

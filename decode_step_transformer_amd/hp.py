@@ -206,7 +206,7 @@ def hp_pack_weight_q4(codes: torch.Tensor, sm: torch.Tensor, k: int, n: int, str
 def hp_pack_weight_f16(w: torch.Tensor, stream=None) -> Mat:
     _need(w, torch.float16, "w")
     k, n = w.shape
-    wt = torch.empty((n, k), dtype=torch.float16, device=w.device)
+    wt = torch.empty(n * k, dtype=torch.float16, device=w.device)  # fragment-major tiles
     _check(lib().hp_pack_weight_f16(_ptr(w), k, n, _ptr(wt), _stream(stream)))
     return Mat(HP_F16, k, n, wt)
 

@@ -82,7 +82,11 @@ enum { HP_F16 = 0, HP_Q4 = 1 };
  * background section).  Weights are grouped along the output-channel
  * dimension ([FlexGen] section 5): a group is w[kk][64 g .. 64 g + 63].
  * Stored in the GEMM layout produced by hp_pack_weight_*:
- *   HP_F16: data = half wt[n][k] (the transpose: k contiguous per output).
+ *   HP_F16: data = half tiles[n/16][k/128][4][64][8]: tile (nb, kb), k-step
+ *           j, lane L (0..63) holds the 8 inputs kk = 128 kb + 32 j +
+ *           8 (L / 16) + e, e = 0..7, of output column n = 16 nb + L % 16
+ *           (the MFMA operand fragments of one k-step are one contiguous
+ *           1 KB).
  *   HP_Q4:  data = u8 tiles[n/16][k/128][64][16]: tile (nb, kb), lane L
  *           (0..63) holds the 32 codes of output column n = 16 nb + L % 16
  *           at inputs kk = 128 kb + 32 (L / 16) + 0..31, as 4 dwords; dword
@@ -164,7 +168,8 @@ hp_status hp_dequantize_g64(const void* codes, const void* sm, int64_t rows, int
 hp_status hp_pack_weight_q4(const void* codes, const void* sm, int32_t k, int32_t n,
                             void* packed, void* scale, void* minv, void* stream);
 
-/* fp16 weight w[k][n] (device) -> the HP_F16 GEMM layout wt[n][k]. */
+/* fp16 weight w[k][n] (device) -> the HP_F16 GEMM layout (see hp_mat;
+ * k * n halves, 16-byte aligned).  Requires k % 128 == 0, n % 64 == 0. */
 hp_status hp_pack_weight_f16(const void* w, int32_t k, int32_t n, void* wt, void* stream);
 
 /* ---------------------------------------------------------- layer stages */
