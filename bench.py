@@ -807,7 +807,8 @@ def main():
 
     # decode-phase kernels
     dec = {}
-    dec_kernel = {"gemm_q4_skinny": "k_gemm_dq", "attn_decode_q4": "k_decode_attn"}
+    dec_kernel = {"gemm_q4_skinny": "k_gemm_dq", "attn_decode_q4": "k_decode_attn",
+                  "gemm_f16_skinny": "k_gemm<", "attn_decode_f16": "k_decode_attn"}
     for kname, (cnt, ms) in dprof.items():
         e = {"launches": cnt, "avg_launch_ms": ms / cnt, "total_ms": ms}
         if kname in dec_kernel:

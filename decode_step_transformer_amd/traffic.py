@@ -52,6 +52,7 @@ COPY_BYTES = 1 << 30
 KERNEL_SOURCES = {
     "k_gemm16": ["csrc/gemm16.hip", "csrc/lds_dma.h", "csrc/common.h"],
     "k_gemm_dq": ["csrc/gemm_dec.hip", "csrc/lds_dma.h", "csrc/dequant_dev.h", "csrc/common.h"],
+    "k_gemm<": ["csrc/gemm.hip", "csrc/common.h"],  # the fp16 skinny product
     "k_decode_attn": ["csrc/attn.hip", "csrc/decode_dev.h", "csrc/dequant_dev.h", "csrc/common.h"],
     "k_topk_attn": ["csrc/topk.hip", "csrc/decode_dev.h", "csrc/dequant_dev.h", "csrc/common.h"],
     "k_multi_attn": ["csrc/attn.hip", "csrc/lds_dma.h", "csrc/dequant_dev.h", "csrc/common.h"],
