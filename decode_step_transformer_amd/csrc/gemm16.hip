@@ -55,8 +55,9 @@ struct G16Args {
 
 // FRAG: the weight is in the fragment-major HP_F16 layout (tile of 16
 // columns x 128 inputs = 4 KB, k-step j's 1 KB holding lane L's 8 inputs
-// 32 j + 8 (L / 16) .. of column L % 16); else rows wt[n][k] (the int4
-// expansion).  Either way a direct load fills the same LDS image.
+// 32 j + 8 (L / 16) .. of column L % 16, the tiles of a k-block adjacent);
+// else rows wt[n][k] (the int4 expansion).  Either way a direct load fills
+// the same LDS image.
 template <bool FRAG>
 __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
   __shared__ __attribute__((aligned(1024))) _Float16 S[G_NS * G_STAGE];
@@ -95,15 +96,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
     srcA[h] = g.A + m * g.lda + 8 * cchunk;
     if constexpr (FRAG) {
       const int64_t nb = min(n0 + 16 * (2 * wave + h), g.N - 16) / 16;
-      srcB[h] = g.W + nb * (g.K / 128) * 2048 + (rin + 16 * cchunk) * 8;
+      srcB[h] = g.W + nb * 2048 + (rin + 16 * cchunk) * 8;
     } else {
       const int64_t n = min(n0 + 16 * (2 * wave + h) + rin, g.N - 1);
       srcB[h] = g.W + n * g.ldw + 8 * cchunk;
     }
   }
+  // fragment-major weights: k-step ks is k-step ks % 4 of k-block ks / 4,
+  // whose tiles (N / 16 of 4 KB) are adjacent
+  auto frag_off = [&](int ks) __attribute__((always_inline)) {
+    return (int64_t)(ks >> 2) * (g.N / 16) * 2048 + (ks & 3) * 512;
+  };
   const uint32_t sbase = lds_off(S);
   auto issue = [&](int ks, int stage) __attribute__((always_inline)) {
-    const int64_t ko = (int64_t)ks * G_BK, kob = FRAG ? (int64_t)ks * 512 : ko;
+    const int64_t ko = (int64_t)ks * G_BK, kob = FRAG ? frag_off(ks) : ko;
     const uint32_t st = sbase + (uint32_t)stage * G_STAGE * 2;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm16(G16Args g) {
     wait_vm<8, 0>();  // this wave's reads of stage kk are done, and its loads of kk+1
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t ko = (int64_t)ck(kk + 4) * G_BK, kob = FRAG ? (int64_t)ck(kk + 4) * 512 : ko;
+    const int64_t ko = (int64_t)ck(kk + 4) * G_BK, kob = FRAG ? frag_off(ck(kk + 4)) : ko;
     const uint32_t stg = sbase + (uint32_t)(kk & 3) * G_STAGE * 2;
     const _Float16* St = S + ((kk + 1) & 3) * G_STAGE;
     const int slot = (kq ^ ((r16 >> 1) & 3)) * 8;

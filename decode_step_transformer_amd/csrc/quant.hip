@@ -103,10 +103,11 @@ __global__ __launch_bounds__(256) void k_pack_sm(const uint32_t* __restrict__ sm
   }
 }
 
-// fp16 w[k][n] -> the fragment-major HP_F16 layout: tile (nb, kb) of 16
-// output columns x 128 inputs is 4 KB contiguous, [j][lane][8] halves, lane
-// L holding column 16 nb + L % 16 at inputs 128 kb + 32 j + 8 (L / 16) + e
-// (exactly one MFMA operand fragment per k-step j).  64 x 64 tiles of w pass
+// fp16 w[k][n] -> the fragment-major HP_F16 layout: tile (kb, nb) of 16
+// output columns x 128 inputs is 4 KB contiguous at (kb (n / 16) + nb) 4 KB,
+// [j][lane][8] halves, lane L holding column 16 nb + L % 16 at inputs
+// 128 kb + 32 j + 8 (L / 16) + e (exactly one MFMA operand fragment per
+// k-step j; the tiles of one k-block are adjacent).  64 x 64 tiles of w pass
 // through LDS; each thread writes 8 consecutive inputs of one column (16 B).
 __global__ __launch_bounds__(256) void k_pack_f16(const uint16_t* __restrict__ w, int32_t k,
                                                   int32_t n, uint16_t* __restrict__ wt) {
@@ -117,11 +118,11 @@ __global__ __launch_bounds__(256) void k_pack_f16(const uint16_t* __restrict__ w
     tile[r][c] = w[(int64_t)(k0 + r) * n + n0 + c];
   }
   __syncthreads();
-  const int64_t KB = k / 128;
+  const int64_t NB = n / 16;
   for (int i = threadIdx.x; i < 64 * 8; i += 256) {
     const int c = i / 8, k8 = (i % 8) * 8;  // column n0 + c, inputs k0 + k8 .. + 7
     const int nn = n0 + c, kk = k0 + k8;
-    const int64_t off = (((int64_t)(nn / 16) * KB + kk / 128) * 4 + (kk % 128) / 32) * 512 +
+    const int64_t off = (((int64_t)(kk / 128) * NB + nn / 16) * 4 + (kk % 128) / 32) * 512 +
                         ((nn % 16) + 16 * ((kk % 32) / 8)) * 8;
     uint32_t v[4];
 #pragma unroll

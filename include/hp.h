@@ -82,11 +82,11 @@ enum { HP_F16 = 0, HP_Q4 = 1 };
  * background section).  Weights are grouped along the output-channel
  * dimension ([FlexGen] section 5): a group is w[kk][64 g .. 64 g + 63].
  * Stored in the GEMM layout produced by hp_pack_weight_*:
- *   HP_F16: data = half tiles[n/16][k/128][4][64][8]: tile (nb, kb), k-step
+ *   HP_F16: data = half tiles[k/128][n/16][4][64][8]: tile (kb, nb), k-step
  *           j, lane L (0..63) holds the 8 inputs kk = 128 kb + 32 j +
  *           8 (L / 16) + e, e = 0..7, of output column n = 16 nb + L % 16
  *           (the MFMA operand fragments of one k-step are one contiguous
- *           1 KB).
+ *           1 KB; the tiles of one k-block are adjacent).
  *   HP_Q4:  data = u8 tiles[n/16][k/128][64][16]: tile (nb, kb), lane L
  *           (0..63) holds the 32 codes of output column n = 16 nb + L % 16
  *           at inputs kk = 128 kb + 32 (L / 16) + 0..31, as 4 dwords; dword
