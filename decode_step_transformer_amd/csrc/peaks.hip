@@ -1,7 +1,9 @@
 // Measurement probes, not part of the layer: what this GPU attains on the two
 // resources the kernels are bound by, as the reference for their fractions.
 //  * k_peak_read streams a buffer once with 16-byte non-temporal loads, four
-//    per lane in flight, grid-stride over 8 workgroups of 256 threads per CU.
+//    per lane in flight, grid-stride over the given number of 256-thread
+//    workgroups (the rate depends on it: at 2 per CU it reads 7.05 TB/s, at
+//    8 per CU 6.0-6.1, measured; fewer streams keep HBM rows open longer).
 //  * k_peak_mfma keeps 16 independent v_mfma_f32_16x16x32_f16 chains per wave
 //    on 8 waves per CU (two per SIMD), operands in registers.
 // Both fold what they read or computed into a value that decides a store, so
