@@ -62,6 +62,20 @@ def unpack_q4_weight(packed, k, n):
     return c
 
 
+def unpack_f16_weight(packed, k, n):
+    """The fragment-major HP_F16 layout of include/hp.h -> w[k][n] (uint16 bits)."""
+    t = packed.reshape(k // 128, n // 16, 4, 64, 8)            # kb, nb, j, lane, e
+    w = np.zeros((k, n), np.uint16)
+    lane = np.arange(64)
+    for kb in range(k // 128):
+        for nb in range(n // 16):
+            cols = 16 * nb + (lane % 16)
+            for j in range(4):
+                for e in range(8):
+                    w[128 * kb + 32 * j + 8 * (lane // 16) + e, cols] = t[kb, nb, j, :, e]
+    return w
+
+
 def check_flips(g_codes, r_codes, what, max_rate):
     """int4 cache rows that the two sides coded from K/V each computed itself (sums in
     different orders): reports the share of differing 4-bit codes (the flip rate),

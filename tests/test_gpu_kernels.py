@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import TOL, assert_close, dev, host, unpack_nibbles, unpack_q4_weight
+from helpers import TOL, assert_close, dev, host, unpack_f16_weight, unpack_nibbles, unpack_q4_weight
 
 pytestmark = pytest.mark.gpu
 SEED = synth.seed_for(99)
@@ -83,6 +83,17 @@ def test_pack_q4_layout(hp, orc, k, n):
     assert np.array_equal(unpack_q4_weight(host(m.data), k, n), unpack_nibbles(rc))
     assert np.array_equal(host(m.scale).view(np.uint16), rs[:, :, 0].T)
     assert np.array_equal(host(m.minv).view(np.uint16), rs[:, :, 1].T)
+
+
+@pytest.mark.parametrize("k,n", [(128, 64), (256, 768), (384, 1024)])
+def test_pack_f16_layout(hp, k, n):
+    """hp_pack_weight_f16 writes the fragment-major layout the header documents,
+    moving every value unchanged; shapes off the 128 x 64 grid are refused."""
+    w = synth.normal_f16(SEED, 40 + k + n, (k, n), 0.02)
+    m = hp.hp_pack_weight_f16(dev(w))
+    assert np.array_equal(unpack_f16_weight(host(m.data).view(np.uint16), k, n), w.view(np.uint16))
+    with pytest.raises(hp.HPError):
+        hp.hp_pack_weight_f16(dev(w[:, : n - 32]))
 
 
 def _ref_gemm(orc, x, w, fmt, res=None, relu=False):
