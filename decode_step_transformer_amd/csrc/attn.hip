@@ -196,7 +196,8 @@ __device__ __forceinline__ int prefix_len(const DecArgs& a, int r) {
 // A chunk of an int4 cache is 3 loads (133 VGPRs, 3 waves per SIMD: the
 // extra rows in flight outweigh the lower occupancy, 3-9% at the 30B decode
 // shape against 2 loads).  PAGED: the cache is reached through a page table
-// (one lookup per load); otherwise rows are contiguous per (request, head).
+// (one page per load, the request's pages held in lanes); otherwise rows are
+// contiguous per (request, head).
 template <int D, bool Q4, bool MASKED, bool PAGED>
 __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   using S = DecShape<D, Q4>;
@@ -219,9 +220,22 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   // last visible one stay in its page: the clamp only applies within the
   // load that holds that row, or to loads past it, whose j is that row).
   const int64_t rowbase = ((int64_t)r * a.H + h) * a.cap;
+  // paged: the request's page numbers (up to 64) sit one per lane, loaded
+  // once, so a load's page comes from a lane read instead of a table load
+  // the cache load would have to wait for
+  const int npg = PAGED ? a.cap / a.PR : 0;
+  int pg_lane = 0;
+  if constexpr (PAGED) {
+    if (npg <= 64 && lane < npg)
+      pg_lane = min(max(a.pages[(int64_t)r * npg + lane], 0), a.pool - 1);
+  }
   auto base = [&](int j) __attribute__((always_inline)) -> int64_t {
     if constexpr (!PAGED) return rowbase;
-    else return cache_row(a.pages, a.PR, a.pool, a.cap, a.H, r, h, j) - j;
+    else {
+      if (npg > 64) return cache_row(a.pages, a.PR, a.pool, a.cap, a.H, r, h, j) - j;
+      const int pg = __builtin_amdgcn_readlane(pg_lane, j / a.PR);
+      return ((int64_t)pg * a.H + h) * a.PR + j % a.PR - j;
+    }
   };
   const int g = Q4 ? (32 * qd) / 64 : 0;  // int4 group of this lane's dims
   const uint32_t lane_off = 16 * qd, lane_soff = 4 * g;
