@@ -79,6 +79,31 @@ def test_paged_cache_matches_contiguous(hp, fmt, heads, h1):
     assert np.array_equal(host(a).view(np.uint16), host(c).view(np.uint16))
 
 
+@pytest.mark.parametrize("cap", [4096, 4224])
+def test_paged_cache_many_pages(hp, cap):
+    """Decode attention over long paged caches: 64 pages per request (the most the
+    kernel holds in lanes) and 66 (table lookups instead), against the contiguous
+    cache bit for bit."""
+    fmt, heads, h1, b, pr = 1, 2, 256, 2, 64
+    D = h1 // heads
+    ppr = cap // pr
+    pool = b * ppr + 3
+    perm = synth.words(SEED, 40 + cap, 0, pool).argsort()[: b * ppr]
+    pages = perm.reshape(b, ppr).astype(np.int32)
+    paged = hp.KVCache(fmt, b, heads, cap, D, page_rows=pr, pool_pages=pool, pages=dev(pages))
+    flat = hp.KVCache(fmt, b, heads, cap, D)
+    T = cap - 70
+    pre = synth.normal_f16(SEED, 50 + cap, (b, T, 3 * h1))
+    for kv in (paged, flat):
+        hp.hp_kv_append(b, T, h1, heads, dev(pre), 0, kv)
+    q = dev(synth.normal_f16(SEED, 60 + cap, (b, 1, 3 * h1)))
+    rpos = np.array([T - 1, T - 1000], np.int32)
+    a = hp.hp_decode_attention_ragged(b, 1, h1, heads, q, dev(rpos), T - 1, paged)
+    c = hp.hp_decode_attention_ragged(b, 1, h1, heads, q, dev(rpos), T - 1, flat)
+    assert np.array_equal(host(a).view(np.uint16), host(c).view(np.uint16))
+    assert np.isfinite(host(a).astype(np.float32)).all()
+
+
 def test_paged_cache_refused_where_unsupported(hp):
     from decode_step_transformer_amd.hp import HPError
     b, heads, h1, cap, pr = 2, 2, 256, 128, 64
