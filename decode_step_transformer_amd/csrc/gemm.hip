@@ -55,7 +55,7 @@ __device__ __forceinline__ void unroll(F&& f) {
 struct GemmArgs {
   const _Float16* A;
   int64_t lda, M;
-  const _Float16* B;  // wt[N][K]
+  const _Float16* B;  // fragment-major fp16 tiles (the HP_F16 layout)
   int K, N, splits, mtiles;  // split s covers k-blocks [s KB / splits, (s+1) KB / splits)
   const _Float16* res;
   int64_t ldr;
