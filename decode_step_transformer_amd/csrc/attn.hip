@@ -461,8 +461,12 @@ __device__ __forceinline__ void flash_store(_Float16* row, float l_lane, const f
   }
 }
 
+// Two workgroups per CU (the LDS ring holds 64 KB at D = 128): the bound
+// caps a lane at 256 registers, so the output accumulators stay in VGPRs
+// (with 512 the compiler put them in AGPRs and moved them through VGPRs for
+// every rescale).
 template <int D>
-__global__ __launch_bounds__(256) void k_prefill_attn(PfArgs a) {
+__global__ __launch_bounds__(256, 2) void k_prefill_attn(PfArgs a) {
   constexpr int KS = D / 32;           // k-steps of the score product
   constexpr int DB = D / 16;           // 16-dim output blocks
   constexpr int RB = 2 * D;            // bytes per key row in LDS
