@@ -393,11 +393,21 @@ __device__ __forceinline__ void flash_block(const uint8_t* Kl, const uint8_t* Vl
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // The running maximum moves only when a score exceeds it by more than 8 in
+  // the exponent (base 2), so the rescale of l and O is rare after the first
+  // blocks; the probabilities, up to 2^8, stay well inside binary16 and the
+  // final division by l removes the common factor.  (The first finite
+  // maximum always moves it: -inf compares as an unbounded rise; an all-
+  // masked lane, -inf to -inf, compares false and keeps probabilities 0.)
   const float m_new = fmaxf(m_run, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float mc = -m_use * c2;
-  const float alpha = __builtin_amdgcn_exp2f(fmaf(m_run, c2, mc));
-  m_run = m_new;
+  if (__any((m_new - m_run) * c2 > 8.f)) {
+    const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c2);
+    m_run = m_new;
+    l_lane *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+  }
+  const float mc = -(m_run == -INFINITY ? 0.f : m_run) * c2;
   float ps = 0.f;
   f16x8 pb[2];
 #pragma unroll
@@ -408,11 +418,7 @@ __device__ __forceinline__ void flash_block(const uint8_t* Kl, const uint8_t* Vl
       ps += p;
       pb[T / 2][4 * (T % 2) + e] = (_Float16)p;
     }
-  l_lane = fmaf(l_lane, alpha, ps);
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-  }
+  l_lane += ps;
   // O^T += V^T P^T over two 32-key steps
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
