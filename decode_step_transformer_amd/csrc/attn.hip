@@ -391,8 +391,7 @@ __device__ __forceinline__ void flash_block(const uint8_t* Kl, const uint8_t* Vl
       if (!visible(k0 + 32 * (T / 2) + 8 * G + 4 * (T % 2) + e)) sc[T][e] = -INFINITY;
       mx = fmaxf(mx, sc[T][e]);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_xor32(max_xor16(mx));
   // The running maximum moves only when a score exceeds it by more than 8 in
   // the exponent (base 2), so the rescale of l and O is rare after the first
   // blocks; the probabilities, up to 2^8, stay well inside binary16 and the
@@ -448,8 +447,7 @@ template <int D, bool PERM = false>
 __device__ __forceinline__ void flash_store(_Float16* row, float l_lane, const f32x4 (&o)[D / 16]) {
   const int G = (threadIdx.x & 63) >> 4;
   // the 4 lanes of a query hold complementary key subsets: total their sums
-  float l = l_lane + __shfl_xor(l_lane, 16);
-  l += __shfl_xor(l, 32);
+  const float l = sum_xor32(sum_xor16(l_lane));
   const float inv = 1.0f / l;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {

@@ -38,6 +38,44 @@ constexpr int DPP_HALF_MIRROR = 0x141;
 constexpr int DPP_MIRROR = 0x140;
 constexpr int DPP_ROR = 0x120;        // + 1..15: rotate right within a row of 16 lanes
 
+// Lane pairs l, l ^ 16 and l, l ^ 32 through gfx950's row swaps
+// (v_permlane16_swap, v_permlane32_swap: vector registers only, no LDS
+// round trip).  Given the same value as both operands, a swap returns the
+// pair's two values, the lower lane's first, in both lanes of the pair.
+__device__ __forceinline__ void pair16(float v, float& lo, float& hi) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  lo = __builtin_bit_cast(float, (uint32_t)r[0]);
+  hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& lo, float& hi) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  lo = __builtin_bit_cast(float, (uint32_t)r[0]);
+  hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+// v + v of lane l ^ 16 (resp. l ^ 32), the same bits in both lanes
+__device__ __forceinline__ float sum_xor16(float v) {
+  float a, b;
+  pair16(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  float a, b;
+  pair32(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  float a, b;
+  pair16(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  float a, b;
+  pair32(v, a, b);
+  return fmaxf(a, b);
+}
+
 // sum over aligned groups of N lanes (N = 1, 2, 4, 8, 16): every lane gets its group's sum
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
@@ -54,6 +92,8 @@ __device__ __forceinline__ float strided_sum(float v) {
   if constexpr (N <= 2) v += dpp<DPP_ROR + 2>(v);
   if constexpr (N <= 4) v += dpp<DPP_ROR + 4>(v);
   if constexpr (N <= 8) v += dpp<DPP_ROR + 8>(v);
+  // (the row swaps measured no faster here: these kernels keep the vector
+  // units busy with the int4 expansion, and the LDS pipe is otherwise idle)
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);
   return v;
