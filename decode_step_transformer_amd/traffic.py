@@ -55,7 +55,8 @@ KERNEL_SOURCES = {
     "k_gemm<": ["csrc/gemm.hip", "csrc/common.h"],  # the fp16 skinny product
     "k_decode_attn": ["csrc/attn.hip", "csrc/decode_dev.h", "csrc/dequant_dev.h", "csrc/common.h"],
     "k_topk_attn": ["csrc/topk.hip", "csrc/decode_dev.h", "csrc/dequant_dev.h", "csrc/common.h"],
-    "k_multi_attn": ["csrc/attn.hip", "csrc/lds_dma.h", "csrc/dequant_dev.h", "csrc/common.h"],
+    "k_multi_attn": ["csrc/attn.hip", "csrc/lds_dma.h", "csrc/decode_dev.h", "csrc/dequant_dev.h",
+                     "csrc/common.h"],
     "k_kv_append": ["csrc/attn.hip", "csrc/quant_dev.h", "csrc/common.h"],
     "k_quantize_g64": ["csrc/quant.hip", "csrc/quant_dev.h", "csrc/common.h"],
 }
