@@ -249,6 +249,59 @@ def test_prefill_attention(hp, orc, D, s, b):
     assert_close(host(out), ref, what="prefill attention")
 
 
+def _ramp_keys(qkv, h1, up):
+    """qkv [b, s, 3 h1] with key row j scaled by 1 + j / 8 (or the reverse order), in binary16."""
+    f = 1.0 + np.arange(qkv.shape[1]) / 8.0
+    if not up:
+        f = f[::-1]
+    out = qkv.copy()
+    out[:, :, h1:2 * h1] = (out[:, :, h1:2 * h1].astype(np.float32) * f[None, :, None]).astype(np.float16)
+    return out
+
+
+@pytest.mark.parametrize("up", [True, False])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_attention_moving_maximum(hp, orc, D, up):
+    """Scores that rise block after block by far more than 2^8 in the exponent (the
+    block step's running maximum moves, rescaling l and O, at every block), or fall
+    (it never moves after the first block)."""
+    b, s, heads = 2, 300, 2
+    h1 = heads * D
+    qkv = _ramp_keys(synth.normal_f16(SEED, 95, (b, s, 3 * h1)), h1, up)
+    out = hp.hp_prefill_attention(b, s, h1, heads, dev(qkv))
+    ref = np.zeros((b, s, h1), np.float16)
+    for r in range(b):
+        for h in range(heads):
+            sl = slice(h * D, (h + 1) * D)
+            K = qkv[r, :, h1 + h * D:h1 + (h + 1) * D]
+            V = qkv[r, :, 2 * h1 + h * D:2 * h1 + (h + 1) * D]
+            ref[r, :, sl] = orc.attention(qkv[r, :, sl], K, V, np.arange(1, s + 1))
+    assert_close(host(out), ref, what="prefill attention, moving maximum")
+
+
+@pytest.mark.parametrize("up", [True, False])
+def test_tree_attention_moving_maximum(hp, orc, up):
+    """The multi-query MFMA path (int4 cache, tree masks) over a prefix whose scores
+    rise or fall across its 64-row blocks as in the prefill case."""
+    b, heads, D, P, q = 2, 2, 128, 300, 64
+    h1 = heads * D
+    pre = _ramp_keys(synth.normal_f16(SEED, 96, (b, P, 3 * h1)), h1, up)
+    kv = hp.KVCache(1, b, heads, P + q, D)
+    hp.hp_kv_append(b, P, h1, heads, dev(pre), 0, kv)
+    qkv = synth.normal_f16(SEED, 97, (b, q, 3 * h1))
+    hp.hp_kv_append(b, q, h1, heads, dev(qkv), P, kv)
+    parents = np.stack([synth.bfs_parents(SEED, 98 + r, q) for r in range(b)])
+    masks = np.stack([orc.tree_masks(p) for p in parents])
+    out = hp.hp_decode_attention(b, q, h1, heads, dev(qkv), P, kv, masks=dev(masks.view(np.int64)))
+    K, V = _cache_values(orc, kv, P + q)
+    ref = np.zeros((b, q, h1), np.float16)
+    for r in range(b):
+        for h in range(heads):
+            ref[r, :, h * D:(h + 1) * D] = orc.attention(qkv[r, :, h * D:(h + 1) * D], K[r, h],
+                                                         V[r, h], [P] * q, masks[r], P)
+    assert_close(host(out), ref, what="tree attention, moving maximum")
+
+
 def test_tree_masks(hp, orc):
     import torch
     b, q = 8, 64
