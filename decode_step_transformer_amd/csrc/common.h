@@ -106,11 +106,14 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
                              int32_t pos, const int32_t* dpos, const int32_t* plen,
                              const uint64_t* masks, const hp_kv& kv, void* out, hipStream_t st);
 // Top-K sparse decode attention (one query per request); visible rows
-// [0, pos + *dpos + 1) with max_t bounding that count (<= 4096); topk = 0
-// keeps ceil(T / 10).  Returns HP_ERR_SHAPE if max_t is out of range.
+// [0, pos + *dpos + 1), or [0, min(rpos[r], pos) + 1) for request r when rpos
+// is given, with max_t bounding that count (<= 4096); topk = 0 keeps
+// ceil(T / 10).  Contiguous or paged caches.  Returns HP_ERR_SHAPE if max_t is
+// out of range.
 hp_status launch_topk_attention(int32_t b, int32_t h1, int32_t heads, const void* qkv, int32_t pos,
                                 const int32_t* dpos, int32_t max_t, int32_t topk, const hp_kv& kv,
-                                void* out, int32_t* idx, hipStream_t st);
+                                void* out, int32_t* idx, hipStream_t st,
+                                const int32_t* rpos = nullptr);
 void launch_tree_masks(int32_t b, int32_t q, const int32_t* parent, uint64_t* masks, int32_t* err,
                        hipStream_t st);
 void launch_tree_prune(int32_t b, int32_t q, int32_t pos, const int32_t* parent,

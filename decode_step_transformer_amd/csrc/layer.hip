@@ -337,7 +337,7 @@ static hp_status decode_body(int b, int q, int h1, int h2, int heads, const hp_l
   if ((r = launch_ok("k_kv_append")) != HP_OK) return r;
   if (topk_max_t > 0) {
     if ((r = launch_topk_attention(b, h1, heads, qkv, pos, dpos, topk_max_t, 0, kv,
-                                   at<void>(ws, L.a), nullptr, st)) != HP_OK)
+                                   at<void>(ws, L.a), nullptr, st, rpos)) != HP_OK)
       return fail(r, "topk attention: bad row count");
     if ((r = launch_ok("k_topk_attn")) != HP_OK) return r;
   } else {
@@ -653,7 +653,7 @@ hp_status hp_topk_attention(int32_t b, int32_t h1, int32_t heads, const void* qk
   if (!qkv || !out) return fail(HP_ERR_NULL, "NULL pointer");
   NEED_ALIGN(qkv, 16);
   NEED_ALIGN(out, 16);
-  hp_status s = check_kv(kv, pos + 1);
+  hp_status s = check_kv(kv, pos + 1, 1);
   if (s != HP_OK) return s;
   if ((s = device_check()) != HP_OK) return s;
   if ((s = launch_topk_attention(b, h1, heads, qkv, pos, nullptr, pos + 1, topk, *kv, out, idx,
@@ -825,7 +825,6 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
   }
   if (paged && kv[0].cap != (int)(cdiv(d->s + d->n, kv[0].page_rows) * kv[0].page_rows))
     return fail(HP_ERR_SHAPE, "paged pools: cap must be s + n rounded up to page_rows");
-  if (paged && (flags & HP_TOPK10)) return fail(HP_ERR_SHAPE, "paged pools take no HP_TOPK10");
   const Ws L = ws_layout(*d);
   if (ws_bytes < L.total) return fail(HP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   const bool rbr = flags & HP_ROW_BY_ROW, mb = flags & HP_MICROBATCH;
@@ -972,7 +971,7 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
           _Float16* out = (j % 2 == 0) ? T1 : T0;
           if ((s = decode_body(M, 1, d->h1, d->h2, d->heads, layers[j], in + r0 * h1,
                                d->s + d->n - 1, nullptr, nullptr, kv_slice(kj, d->heads, D, r0),
-                               out + r0 * h1, ws, L, st, 0, rpos)) != HP_OK)
+                               out + r0 * h1, ws, L, st, topk_max_t, rpos)) != HP_OK)
             return finish(s);
         }
       }

@@ -18,6 +18,10 @@
 //  3. The kept V rows are gathered (two register sets in flight) and summed
 //     with weights exp(z - max); the maximum is the top score, known before
 //     the pass, so no rescaling is needed.
+// Paged caches (PAGED): the request's page numbers (up to 64) sit one per
+// lane; a K load's rows lie in one page (RPI rows from a multiple of RPI,
+// RPI | 64 | page rows), read with v_readlane, and every gathered V row looks
+// up its own page (a lane shuffle, or the table in memory past 64 pages).
 #include <math.h>
 
 #include <type_traits>
@@ -40,6 +44,9 @@ struct TopkArgs {
   const uint32_t* vsm;
   _Float16* out;  // [b][h1]
   int32_t* idx;   // [b][H][K] kept rows in ascending order, or null
+  const int32_t* rpos;   // each request's own row of its new token (at most pos), or null
+  const int32_t* pages;  // page table [b][cap / PR] of a paged cache (PAGED)
+  int PR, pool;
 };
 
 // Order-preserving key of a score: a larger score gives a larger key; -0 and
@@ -60,22 +67,28 @@ __device__ __forceinline__ int wave_total(int v) {
          __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
-// This lane's 16-byte slices (and scale/min pairs) of the cache rows row[u].
+// This lane's 16-byte slices (and scale/min pairs) of the cache rows row[u]:
+// rel[u] is the cache row of logical row row[u], less row[u] (the request's
+// first row for a contiguous cache).
 template <int D, bool Q4, int U>
-__device__ __forceinline__ void load_rows(DecPart<U, Q4>& X, const uint8_t* cb, const uint8_t* sb,
-                                          const int (&row)[U], uint32_t lane_off,
-                                          uint32_t lane_soff) {
+__device__ __forceinline__ void load_rows(DecPart<U, Q4>& X, const uint8_t* cache, const uint8_t* smc,
+                                          const int64_t (&rel)[U], const int (&row)[U],
+                                          uint32_t lane_off, uint32_t lane_soff) {
   using S = DecShape<D, Q4>;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    const uint8_t* cb = cache + rel[u] * S::RB;
     X.c[u] = __builtin_nontemporal_load((const u32x4*)(cb + ((uint32_t)row[u] * S::RB + lane_off)));
-    if constexpr (Q4) X.sm[u] = *(const uint32_t*)(sb + ((uint32_t)row[u] * (4 * S::G) + lane_soff));
+    if constexpr (Q4) {
+      const uint8_t* sb = smc + rel[u] * (4 * S::G);
+      X.sm[u] = *(const uint32_t*)(sb + ((uint32_t)row[u] * (4 * S::G) + lane_soff));
+    }
   }
   asm volatile("" ::: "memory");  // keeps each prefetch where it is issued
 }
 
 // NS: score slots per lane (T <= 64 NS)
-template <int D, bool Q4, int NS>
+template <int D, bool Q4, int NS, bool PAGED>
 __global__ __launch_bounds__(64) void k_topk_attn(TopkArgs a) {
   using S = DecShape<D, Q4>;
   constexpr int LPR = S::LPR, RPI = S::RPI, RB = S::RB, G = S::G;
@@ -87,13 +100,34 @@ __global__ __launch_bounds__(64) void k_topk_attn(TopkArgs a) {
   const int lane = threadIdx.x;
   const int qd = lane % LPR, rho = lane / LPR;
   const int h = blockIdx.x % a.H, r = blockIdx.x / a.H;
-  const int T = a.pos + (a.dpos ? *a.dpos : 0) + 1;
+  const int T = a.rpos ? min(max(a.rpos[r], 0), a.pos) + 1 : a.pos + (a.dpos ? *a.dpos : 0) + 1;
   const int K = a.topk > 0 ? min(a.topk, T) : (T + 9) / 10;
   const int64_t rowbase = ((int64_t)r * a.H + h) * a.cap;
-  const uint8_t* kb = (const uint8_t*)a.k + rowbase * RB;
-  const uint8_t* vb = (const uint8_t*)a.v + rowbase * RB;
-  const uint8_t* ksb = (const uint8_t*)(a.ksm + rowbase * G);
-  const uint8_t* vsb = (const uint8_t*)(a.vsm + rowbase * G);
+  const uint8_t* kb = (const uint8_t*)a.k;
+  const uint8_t* vb = (const uint8_t*)a.v;
+  const uint8_t* ksb = (const uint8_t*)a.ksm;
+  const uint8_t* vsb = (const uint8_t*)a.vsm;
+  const int npg = PAGED ? a.cap / a.PR : 0;
+  int pg_lane = 0;
+  if constexpr (PAGED) {
+    if (npg <= 64 && lane < npg) pg_lane = min(max(a.pages[(int64_t)r * npg + lane], 0), a.pool - 1);
+  }
+  // cache row of logical row j, less j: j wave-uniform (a K load), or per lane
+  // (a gathered V row)
+  auto page_row = [&](int pg, int j) __attribute__((always_inline)) -> int64_t {
+    return ((int64_t)pg * a.H + h) * a.PR + j % a.PR - j;
+  };
+  auto table = [&](int j) __attribute__((always_inline)) {
+    return min(max(a.pages[(int64_t)r * npg + j / a.PR], 0), a.pool - 1);
+  };
+  auto rel_uniform = [&](int j) __attribute__((always_inline)) -> int64_t {
+    if constexpr (!PAGED) return rowbase;
+    else return page_row(npg > 64 ? table(j) : __builtin_amdgcn_readlane(pg_lane, j / a.PR), j);
+  };
+  auto rel_lane = [&](int j) __attribute__((always_inline)) -> int64_t {
+    if constexpr (!PAGED) return rowbase;
+    else return page_row(npg > 64 ? table(j) : __shfl(pg_lane, j / a.PR), j);
+  };
   const int g = Q4 ? (32 * qd) / 64 : 0;
   const uint32_t lane_off = 16 * qd, lane_soff = 4 * g;
   const DqConst dq{0x000F000Fu, 0x00F000F0u, in_vgpr(0x64006400u), in_vgpr(0x54005400u)};
@@ -101,11 +135,17 @@ __global__ __launch_bounds__(64) void k_topk_attn(TopkArgs a) {
   Q.load(a.qkv + (int64_t)r * 3 * a.h1 + h * D + (Q4 ? 32 : 8) * qd);
 
   // ---- pass 1: scores
+  // rows past the visible range are clamped to its last row; the rows of one
+  // load stay in the page of its first row (or of that last row)
   auto load_k = [&](DecPart<UK, Q4>& X, int c) {
     int row[UK];
+    int64_t rel[UK];
 #pragma unroll
-    for (int u = 0; u < UK; ++u) row[u] = min(c * CRK + rho + RPI * u, T - 1);
-    load_rows<D, Q4>(X, kb, ksb, row, lane_off, lane_soff);
+    for (int u = 0; u < UK; ++u) {
+      row[u] = min(c * CRK + rho + RPI * u, T - 1);
+      rel[u] = rel_uniform(min(c * CRK + RPI * u, T - 1));
+    }
+    load_rows<D, Q4>(X, kb, ksb, rel, row, lane_off, lane_soff);
   };
   auto score = [&](const DecPart<UK, Q4>& X, int c) {
 #pragma unroll
@@ -203,13 +243,15 @@ __global__ __launch_bounds__(64) void k_topk_attn(TopkArgs a) {
   float l_lane = 0.f;
   auto load_v = [&](DecPart<UV, Q4>& X, float (&z)[UV], int c) {
     int row[UV];
+    int64_t rel[UV];
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       const int e = c * CRV + rho + RPI * u;
       row[u] = sel[min(e, K - 1)];
       z[u] = e < K ? sc[row[u]] : -INFINITY;  // list slots past K weigh 0
+      rel[u] = rel_lane(row[u]);
     }
-    load_rows<D, Q4>(X, vb, vsb, row, lane_off, lane_soff);
+    load_rows<D, Q4>(X, vb, vsb, rel, row, lane_off, lane_soff);
   };
   auto accumulate = [&](const DecPart<UV, Q4>& X, const float (&z)[UV]) {
     float p[UV];
@@ -243,26 +285,29 @@ constexpr int TOPK_MAX_T = 4096;
 
 hp_status launch_topk_attention(int32_t b, int32_t h1, int32_t heads, const void* qkv, int32_t pos,
                                 const int32_t* dpos, int32_t max_t, int32_t topk, const hp_kv& kv,
-                                void* out, int32_t* idx, hipStream_t st) {
+                                void* out, int32_t* idx, hipStream_t st, const int32_t* rpos) {
   if (max_t < 1 || max_t > TOPK_MAX_T) return HP_ERR_SHAPE;
   const int D = h1 / heads;
+  const bool paged = kv.page_rows > 0;
   TopkArgs a{(const _Float16*)qkv, h1,   heads, pos,  dpos, topk,
              kv.cap,               kv.k, kv.v,  (const uint32_t*)kv.k_sm,
-             (const uint32_t*)kv.v_sm, (_Float16*)out, idx};
+             (const uint32_t*)kv.v_sm, (_Float16*)out, idx, rpos,
+             paged ? kv.pages : nullptr, kv.page_rows, kv.pool_pages};
   const dim3 grid((unsigned)((int64_t)b * heads));
   Prof prof(kv.fmt == HP_Q4 ? "attn_topk_q4" : "attn_topk_f16", st);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, a); };
   auto by_ns = [&](auto d, auto q4) {
     constexpr int DD = decltype(d)::value;
     constexpr bool QQ = decltype(q4)::value;
-    if (max_t <= 256) go(k_topk_attn<DD, QQ, 4>);
-    else if (max_t <= 512) go(k_topk_attn<DD, QQ, 8>);
-    else if (max_t <= 768) go(k_topk_attn<DD, QQ, 12>);
-    else if (max_t <= 1024) go(k_topk_attn<DD, QQ, 16>);
-    else if (max_t <= 1536) go(k_topk_attn<DD, QQ, 24>);
-    else if (max_t <= 2048) go(k_topk_attn<DD, QQ, 32>);
-    else if (max_t <= 3072) go(k_topk_attn<DD, QQ, 48>);
-    else go(k_topk_attn<DD, QQ, 64>);
+    auto pick = [&](auto kc, auto kp) { paged ? go(kp) : go(kc); };
+    if (max_t <= 256) pick(k_topk_attn<DD, QQ, 4, false>, k_topk_attn<DD, QQ, 4, true>);
+    else if (max_t <= 512) pick(k_topk_attn<DD, QQ, 8, false>, k_topk_attn<DD, QQ, 8, true>);
+    else if (max_t <= 768) pick(k_topk_attn<DD, QQ, 12, false>, k_topk_attn<DD, QQ, 12, true>);
+    else if (max_t <= 1024) pick(k_topk_attn<DD, QQ, 16, false>, k_topk_attn<DD, QQ, 16, true>);
+    else if (max_t <= 1536) pick(k_topk_attn<DD, QQ, 24, false>, k_topk_attn<DD, QQ, 24, true>);
+    else if (max_t <= 2048) pick(k_topk_attn<DD, QQ, 32, false>, k_topk_attn<DD, QQ, 32, true>);
+    else if (max_t <= 3072) pick(k_topk_attn<DD, QQ, 48, false>, k_topk_attn<DD, QQ, 48, true>);
+    else pick(k_topk_attn<DD, QQ, 64, false>, k_topk_attn<DD, QQ, 64, true>);
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;

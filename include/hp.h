@@ -124,9 +124,10 @@ typedef struct {
  * j % page_rows of page pages[r * (cap / page_rows) + j / page_rows]
  * (device int32 [b][cap / page_rows]; entries outside [0, pool_pages) are
  * clamped into it).  cap is then the logical rows per request, a multiple
- * of page_rows; page_rows is a multiple of 64.  hp_kv_append and
- * hp_decode_attention / hp_decode_attention_ragged with q < 16 take paged
- * caches; the other cache calls return HP_ERR_SHAPE for them.  Under
+ * of page_rows; page_rows is a multiple of 64.  hp_kv_append,
+ * hp_decode_attention / hp_decode_attention_ragged with q < 16 and
+ * hp_topk_attention take paged caches; the other cache calls return
+ * HP_ERR_SHAPE for them.  Under
  * HP_DIAGONAL, hp_run_block assigns the pages itself (pages = NULL; see
  * HP_DIAGONAL).  Contiguous caches: pages = NULL, page_rows = pool_pages
  * = 0. */
@@ -256,7 +257,8 @@ hp_status hp_decode_attention_ragged(int32_t b, int32_t q, int32_t h1, int32_t h
  * ceil((pos + 1) / 10) when topk == 0.  qkv: device half [b][3 h1] (query in
  * columns [0, h1)); out: device half [b][h1]; idx: device int32
  * [b][heads][K] receiving the kept rows in ascending order, or NULL.
- * Requires pos + 1 <= min(kv->cap, 4096). */
+ * Contiguous or paged caches (see hp_kv).  Requires pos + 1 <= min(kv->cap,
+ * 4096). */
 hp_status hp_topk_attention(int32_t b, int32_t h1, int32_t heads, const void* qkv, int32_t pos,
                             int32_t topk, const hp_kv* kv, void* out, int32_t* idx, void* stream);
 
@@ -379,8 +381,8 @@ enum {
                           page's peak-memory formula instead of b (s + n)
                           rows; hp_diagonal_pages() gives the pages needed.
                           One product, append and attention per layer and
-                          iteration for all live batches.  Not with
-                          HP_TOPK10. */
+                          iteration for all live batches (with HP_TOPK10,
+                          Top-K attention over each request's own rows). */
 };
 
 /* [FlexGen] section 4, Algorithm 1: zig-zag block schedule over one block of

@@ -112,8 +112,32 @@ def test_paged_cache_refused_where_unsupported(hp):
     q = dev(synth.normal_f16(SEED, 40, (b, 16, 3 * h1)))
     with pytest.raises(HPError):  # int4 with q >= 16 runs on the multi-query kernel
         hp.hp_decode_attention(b, 16, h1, heads, q, 32, kv)
-    with pytest.raises(HPError):
-        hp.hp_topk_attention(b, h1, heads, q[:, 0].contiguous(), 32, kv)
+
+
+@pytest.mark.parametrize("fmt", [1, 0])
+@pytest.mark.parametrize("cap,T", [(256, 200), (4224, 4000)])
+def test_paged_topk_matches_contiguous(hp, fmt, cap, T):
+    """Top-K sparse attention through a shuffled page table (4 pages per request:
+    page numbers held in lanes; 66: table lookups) against the contiguous cache:
+    the same kept rows and the same outputs, bit for bit."""
+    heads, h1, b, pr = 2, 256, 3, 64
+    D = h1 // heads
+    ppr = cap // pr
+    pool = b * ppr + 3
+    perm = synth.words(SEED, 70 + cap + fmt, 0, pool).argsort()[: b * ppr]
+    pages = perm.reshape(b, ppr).astype(np.int32)
+    paged = hp.KVCache(fmt, b, heads, cap, D, page_rows=pr, pool_pages=pool, pages=dev(pages))
+    flat = hp.KVCache(fmt, b, heads, cap, D)
+    pre = synth.normal_f16(SEED, 80 + cap + fmt, (b, T, 3 * h1))
+    for kv in (paged, flat):
+        hp.hp_kv_append(b, T, h1, heads, dev(pre), 0, kv)
+    q = dev(synth.normal_f16(SEED, 90 + cap + fmt, (b, 3 * h1)))
+    for topk in (0, 7):
+        oa, ia = hp.hp_topk_attention(b, h1, heads, q, T - 1, paged, topk=topk, idx=True)
+        oc, ic = hp.hp_topk_attention(b, h1, heads, q, T - 1, flat, topk=topk, idx=True)
+        assert np.array_equal(host(ia), host(ic))
+        assert np.array_equal(host(oa).view(np.uint16), host(oc).view(np.uint16))
+        assert np.isfinite(host(oa).astype(np.float32)).all()
 
 
 def _block(hp, d, l, seed, fmt=1):
@@ -175,3 +199,29 @@ def test_diagonal_paged_pool(hp, b, s, n, gbs):
     with pytest.raises(HPError) as e:
         _run(hp, d, layers, x, t, small, hp.HP_DIAGONAL)
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("b,s,n,gbs", [(60, 40, 9, 4), (48, 100, 40, 2)])
+def test_diagonal_paged_pool_topk(hp, b, s, n, gbs):
+    """HP_DIAGONAL | HP_TOPK10 with page pools (Top-K attention over each live
+    request's own rows, through the pool's page table) gives the contiguous-slot
+    schedule's outputs bit for bit."""
+    import torch
+    h1, h2, heads, l, pr = 128, 256, 2, 2, 64
+    D = h1 // heads
+    d = hp.dims(b, s, n, h1, h2, l, heads, gbs)
+    layers, x, t = _block(hp, d, l, 11)
+    nb = b // gbs
+    nslot = min(nb, n + 1)
+    slots = [hp.KVCache(1, nslot * gbs, heads, s + n, D) for _ in range(l)]
+    sx, st = _run(hp, d, layers, x, t, slots, hp.HP_DIAGONAL | hp.HP_TOPK10)
+    pages = hp.hp_diagonal_pages(d, pr)
+    cap = -(-(s + n) // pr) * pr
+    pools = [hp.KVCache(1, b, heads, cap, D, page_rows=pr, pool_pages=pages) for _ in range(l)]
+    px, pt = _run(hp, d, layers, x, t, pools, hp.HP_DIAGONAL | hp.HP_TOPK10)
+    assert torch.equal(px.view(torch.int16), sx.view(torch.int16))
+    assert torch.equal(pt.view(torch.int16), st.view(torch.int16))
+    assert bool(torch.isfinite(pt.float()).all())
+    # and the dense-attention schedule differs (Top-K drops rows)
+    _, dt = _run(hp, d, layers, x, t, pools, hp.HP_DIAGONAL)
+    assert not torch.equal(dt.view(torch.int16), pt.view(torch.int16))
