@@ -44,16 +44,18 @@ struct AppendArgs {
   uint32_t* ksm;
   uint32_t* vsm;
   const int32_t* pages;  // paged cache: page table [b][cap / PR], or NULL
-  int PR, pool;          // rows per page, pages in the pool
+  int PR, pool;          // rows per page (a power of two), pages in the pool
 };
 
 // Physical cache row (in rows of one head) of logical row j of request r,
-// head h: contiguous [b][H][cap], or paged [page][H][PR] through the table.
+// head h: contiguous [b][H][cap], or paged [page][H][PR] through the table
+// (PR a power of two: shifts, not divisions).
 __device__ __forceinline__ int64_t cache_row(const int32_t* pages, int PR, int pool, int cap,
                                              int H, int r, int h, int j) {
   if (!pages) return ((int64_t)r * H + h) * cap + j;
-  const int pg = min(max(pages[(int64_t)r * (cap / PR) + j / PR], 0), pool - 1);
-  return ((int64_t)pg * H + h) * PR + j % PR;
+  const int sh = __builtin_ctz(PR);
+  const int pg = min(max(pages[(int64_t)r * (cap >> sh) + (j >> sh)], 0), pool - 1);
+  return ((int64_t)pg * H + h) * PR + (j & (PR - 1));
 }
 
 constexpr int AU = 4;
@@ -195,11 +197,13 @@ __device__ __forceinline__ int prefix_len(const DecArgs& a, int r) {
 
 // A chunk of an int4 cache is 3 loads (133 VGPRs, 3 waves per SIMD: the
 // extra rows in flight outweigh the lower occupancy, 3-9% at the 30B decode
-// shape against 2 loads).  PAGED: the cache is reached through a page table
-// (one page per load, the request's pages held in lanes); otherwise rows are
-// contiguous per (request, head).
-template <int D, bool Q4, bool MASKED, bool PAGED>
+// shape against 2 loads).  PG: 0 = rows contiguous per (request, head);
+// 1 = a paged cache of at most 64 pages per request, their numbers held in
+// lanes; 2 = more pages, the table read from memory per load (one page per
+// load either way).
+template <int D, bool Q4, bool MASKED, int PG>
 __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
+  constexpr bool PAGED = PG > 0;
   using S = DecShape<D, Q4>;
   constexpr int LPR = S::LPR, RPI = S::RPI, RB = S::RB, G = S::G;
   // a chunk is U loads of RPI rows for K and for V; the next chunk is loaded
@@ -223,18 +227,19 @@ __global__ __launch_bounds__(64) void k_decode_attn(DecArgs a) {
   // paged: the request's page numbers (up to 64) sit one per lane, loaded
   // once, so a load's page comes from a lane read instead of a table load
   // the cache load would have to wait for
-  const int npg = PAGED ? a.cap / a.PR : 0;
+  const int prs = PAGED ? __builtin_ctz(a.PR) : 0;  // page rows are a power of two
+  const int npg = PAGED ? a.cap >> prs : 0;
   int pg_lane = 0;
-  if constexpr (PAGED) {
-    if (npg <= 64 && lane < npg)
-      pg_lane = min(max(a.pages[(int64_t)r * npg + lane], 0), a.pool - 1);
+  if constexpr (PG == 1) {
+    if (lane < npg) pg_lane = min(max(a.pages[(int64_t)r * npg + lane], 0), a.pool - 1);
   }
   auto base = [&](int j) __attribute__((always_inline)) -> int64_t {
-    if constexpr (!PAGED) return rowbase;
+    if constexpr (PG == 0) return rowbase;
+    else if constexpr (PG == 2) return cache_row(a.pages, a.PR, a.pool, a.cap, a.H, r, h, j) - j;
     else {
-      if (npg > 64) return cache_row(a.pages, a.PR, a.pool, a.cap, a.H, r, h, j) - j;
-      const int pg = __builtin_amdgcn_readlane(pg_lane, j / a.PR);
-      return ((int64_t)pg * a.H + h) * a.PR + j % a.PR - j;
+      const int jp = j >> prs;  // the page slot of row j: base = (page's first row) - (jp PR)
+      const int pg = __builtin_amdgcn_readlane(pg_lane, jp);
+      return ((int64_t)pg * a.H + h - jp) * a.PR;
     }
   };
   const int g = Q4 ? (32 * qd) / 64 : 0;  // int4 group of this lane's dims
@@ -771,9 +776,11 @@ void launch_decode_attention(int32_t b, int32_t q, int32_t h1, int32_t heads, co
     constexpr int Dd = decltype(d_)::value;
     constexpr bool Qq = decltype(q4_)::value;
     if (paged)
-      m ? go(k_decode_attn<Dd, Qq, true, true>) : go(k_decode_attn<Dd, Qq, false, true>);
+      a.cap / a.PR <= 64
+          ? (m ? go(k_decode_attn<Dd, Qq, true, 1>) : go(k_decode_attn<Dd, Qq, false, 1>))
+          : (m ? go(k_decode_attn<Dd, Qq, true, 2>) : go(k_decode_attn<Dd, Qq, false, 2>));
     else
-      m ? go(k_decode_attn<Dd, Qq, true, false>) : go(k_decode_attn<Dd, Qq, false, false>);
+      m ? go(k_decode_attn<Dd, Qq, true, 0>) : go(k_decode_attn<Dd, Qq, false, 0>);
   };
   using I128 = std::integral_constant<int, 128>;
   using I64 = std::integral_constant<int, 64>;

@@ -234,8 +234,9 @@ static hp_status check_kv(const hp_kv* kv, int need_rows, int paged = 0) {
     return HP_OK;
   }
   if (paged == 0) return fail(HP_ERR_SHAPE, "kv: this call takes contiguous caches only");
-  if (kv->page_rows < 0 || kv->page_rows % 64 || kv->cap % kv->page_rows || kv->pool_pages <= 0)
-    return fail(HP_ERR_SHAPE, "kv: page_rows must be a positive multiple of 64 dividing cap, "
+  if (kv->page_rows < 64 || (kv->page_rows & (kv->page_rows - 1)) || kv->cap % kv->page_rows ||
+      kv->pool_pages <= 0)
+    return fail(HP_ERR_SHAPE, "kv: page_rows must be a power of two >= 64 dividing cap, "
                 "pool_pages positive (page_rows %d, cap %d, pool %d)", kv->page_rows, kv->cap,
                 kv->pool_pages);
   if (paged == 1 && !kv->pages) return fail(HP_ERR_NULL, "kv: paged cache without a page table");
@@ -1130,7 +1131,7 @@ int32_t hp_profile_read(char* buf, size_t len) {
 }
 
 int64_t hp_diagonal_pages(const hp_dims* d, int32_t page_rows) {
-  if (check_dims(d) != HP_OK || page_rows <= 0 || page_rows % 64) return 0;
+  if (check_dims(d) != HP_OK || page_rows < 64 || (page_rows & (page_rows - 1))) return 0;
   const int cap = (int)(cdiv(d->s + d->n, page_rows) * page_rows);
   return diag_page_plan(*d, page_rows, cap, nullptr);
 }

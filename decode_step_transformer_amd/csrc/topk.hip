@@ -107,26 +107,28 @@ __global__ __launch_bounds__(64) void k_topk_attn(TopkArgs a) {
   const uint8_t* vb = (const uint8_t*)a.v;
   const uint8_t* ksb = (const uint8_t*)a.ksm;
   const uint8_t* vsb = (const uint8_t*)a.vsm;
-  const int npg = PAGED ? a.cap / a.PR : 0;
+  const int prs = PAGED ? __builtin_ctz(a.PR) : 0;  // page rows are a power of two
+  const int npg = PAGED ? a.cap >> prs : 0;
   int pg_lane = 0;
   if constexpr (PAGED) {
     if (npg <= 64 && lane < npg) pg_lane = min(max(a.pages[(int64_t)r * npg + lane], 0), a.pool - 1);
   }
   // cache row of logical row j, less j: j wave-uniform (a K load), or per lane
   // (a gathered V row)
+  // (page's first row) - (page slot of j) x (page rows)
   auto page_row = [&](int pg, int j) __attribute__((always_inline)) -> int64_t {
-    return ((int64_t)pg * a.H + h) * a.PR + j % a.PR - j;
+    return ((int64_t)pg * a.H + h - (j >> prs)) * a.PR;
   };
   auto table = [&](int j) __attribute__((always_inline)) {
-    return min(max(a.pages[(int64_t)r * npg + j / a.PR], 0), a.pool - 1);
+    return min(max(a.pages[(int64_t)r * npg + (j >> prs)], 0), a.pool - 1);
   };
   auto rel_uniform = [&](int j) __attribute__((always_inline)) -> int64_t {
     if constexpr (!PAGED) return rowbase;
-    else return page_row(npg > 64 ? table(j) : __builtin_amdgcn_readlane(pg_lane, j / a.PR), j);
+    else return page_row(npg > 64 ? table(j) : __builtin_amdgcn_readlane(pg_lane, j >> prs), j);
   };
   auto rel_lane = [&](int j) __attribute__((always_inline)) -> int64_t {
     if constexpr (!PAGED) return rowbase;
-    else return page_row(npg > 64 ? table(j) : __shfl(pg_lane, j / a.PR), j);
+    else return page_row(npg > 64 ? table(j) : __shfl(pg_lane, j >> prs), j);
   };
   const int g = Q4 ? (32 * qd) / 64 : 0;
   const uint32_t lane_off = 16 * qd, lane_soff = 4 * g;

@@ -124,7 +124,7 @@ typedef struct {
  * j % page_rows of page pages[r * (cap / page_rows) + j / page_rows]
  * (device int32 [b][cap / page_rows]; entries outside [0, pool_pages) are
  * clamped into it).  cap is then the logical rows per request, a multiple
- * of page_rows; page_rows is a multiple of 64.  hp_kv_append,
+ * of page_rows; page_rows is a power of two, at least 64.  hp_kv_append,
  * hp_decode_attention / hp_decode_attention_ragged with q < 16 and
  * hp_topk_attention take paged caches; the other cache calls return
  * HP_ERR_SHAPE for them.  Under
@@ -402,7 +402,8 @@ hp_status hp_run_block(const hp_dims* d, const hp_layer* layers, const void* x, 
                        uint32_t flags, float* times_ms, void* stream);
 
 /* [FlexGen] appendix A.2 (diagonal block schedule, peak memory): the number of
- * cache pages of page_rows rows (per request, all heads; a multiple of 64)
+ * cache pages of page_rows rows (per request, all heads; a power of two, at
+ * least 64)
  * that HP_DIAGONAL with paged caches holds at its peak for these dims: live
  * requests hold ceil(current length / page_rows) pages each.  0 for invalid
  * dims or page_rows. */

@@ -119,6 +119,8 @@ def test_diagonal_pages():
                              (40, 100, 300, 2, 128), (512, 32, 480, 1, 64)):
         d = hp.dims(b, s, n, 256, 512, 2, 4, gbs)
         assert hp.hp_diagonal_pages(d, pr) == _diag_pages_closed_form(b, s, n, gbs, pr), (b, s, n)
+    d = hp.dims(12, 20, 7, 256, 512, 2, 4, 3)
+    assert hp.hp_diagonal_pages(d, 192) == 0 and hp.hp_diagonal_pages(d, 32) == 0  # not a power of two >= 64
     d = hp.dims(512, 32, 480, 256, 512, 2, 4, 1)
     live = 481                                         # n + 1 requests in steady state
     full = live * (32 + 480)                           # their rows at full length

@@ -112,6 +112,11 @@ def test_paged_cache_refused_where_unsupported(hp):
     q = dev(synth.normal_f16(SEED, 40, (b, 16, 3 * h1)))
     with pytest.raises(HPError):  # int4 with q >= 16 runs on the multi-query kernel
         hp.hp_decode_attention(b, 16, h1, heads, q, 32, kv)
+    # page sizes are powers of two (a multiple of 64 that is not one is refused)
+    odd = hp.KVCache(1, b, heads, 384, h1 // heads, page_rows=192, pool_pages=4,
+                     pages=dev(np.arange(b * 2, dtype=np.int32).reshape(b, 2)))
+    with pytest.raises(HPError):
+        hp.hp_kv_append(b, 1, h1, heads, q[:, :1].contiguous(), 0, odd)
 
 
 @pytest.mark.parametrize("fmt", [1, 0])
